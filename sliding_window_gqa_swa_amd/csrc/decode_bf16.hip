@@ -1,0 +1,244 @@
+// Single-token sliding-window GQA decode over the rolling buffer, bf16, gfx950.
+//
+// Mistral 7B (Chinese translation), section 2: tokens are generated one at a
+// time (paragraph "Pre-fill and Chunking"); the keys/values of the last W
+// positions sit in the W slots of the ring (paragraph "Rolling Buffer Cache");
+// the query attends to those W positions (paragraph "Sliding Window
+// Attention").  Section 1: with grouped-query attention the G query heads of
+// a KV head read the same keys and values, which is what makes decoding
+// cheaper in memory.
+//
+// After position pos has been written, slots [0, min(pos+1, W)) hold exactly
+// positions max(0, pos-W+1) .. pos, so the query attends to every valid slot;
+// softmax attention is a sum over keys and needs no slot -> position map.
+//
+// Design (HBM-bound: 4 FLOP per byte of K/V):
+//   * One workgroup = (sequence, KV head, split of the window): 4 waves.  All
+//     G query heads are served from the same loaded K/V rows (GQA sharing).
+//   * Loads: 8 lanes per 256-byte row, two 16-byte loads per lane (one per
+//     128-byte half): each wave-wide load instruction reads whole cache lines
+//     of 8 consecutive rows; a wave streams 32 rows (16 KiB of K+V) per step.
+//   * Scores: v_dot2_f32_bf16 on packed pairs, then a 3-step DPP sum over the
+//     8 lanes of a row; online softmax with one max per head per wave (shared
+//     by all lanes), exp2 with the scale folded in.
+//   * Merge: lane groups by DPP/permute sums, waves through LDS with a
+//     log-sum-exp merge, splits through the workspace + a combine kernel.
+#include "device_common.h"
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerStep = 32;
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
+  __shared__ float sm_acc[kWaves][G][kD];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 3, c = lane & 7;
+  const int splits = p.splits;
+  const int sp = blockIdx.x % splits;
+  const int bg = blockIdx.x / splits;
+  const int hkv = p.cache.n_kv_heads;
+  const int g = bg % hkv, b = bg / hkv;
+  const int W = p.cache.window;
+  const int hq = p.n_q_heads;
+
+  const int pos = p.seq.start_pos[b];
+  const int n_valid = min(pos + 1, W);
+  const int crow = p.seq.cache_idx ? p.seq.cache_idx[b] : b;
+  const int r_begin = sp * p.split_len;
+  const int r_end = min(r_begin + p.split_len, n_valid);
+  const float cs = p.scale_log2;
+
+  const size_t ring0 = ((size_t)crow * hkv + g) * (size_t)W * kD;
+  const uint16_t *kring = (const uint16_t *)p.cache.k + ring0;
+  const uint16_t *vring = (const uint16_t *)p.cache.v + ring0;
+
+  // query slices of the G heads matching this lane's two 8-element chunks
+  u32x4 qa[G], qb[G];
+  const uint16_t *Q = (const uint16_t *)p.q;
+#pragma unroll
+  for (int hh = 0; hh < G; hh++) {
+    const uint16_t *qrow = Q + ((size_t)b * hq + g * G + hh) * kD;
+    qa[hh] = *(const u32x4 *)(qrow + 8 * c);
+    qb[hh] = *(const u32x4 *)(qrow + 64 + 8 * c);
+  }
+
+  float m[G], l[G], acc[G][16];
+#pragma unroll
+  for (int hh = 0; hh < G; hh++) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e++) acc[hh][e] = 0.f;
+  }
+
+  for (int r0 = r_begin + kRowsPerStep * wave; r0 < r_end; r0 += kRowsPerStep * kWaves) {
+    u32x4 ka[4], kb[4], va[4], vb[4];
+    bool ok[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int r = r0 + 8 * k + grp;
+      ok[k] = r < r_end;
+      const u32x4 z = {0, 0, 0, 0};
+      ka[k] = z; kb[k] = z; va[k] = z; vb[k] = z;
+      if (ok[k]) {
+        const uint16_t *kr = kring + (size_t)r * kD;
+        const uint16_t *vr = vring + (size_t)r * kD;
+        ka[k] = __builtin_nontemporal_load((const u32x4 *)(kr + 8 * c));
+        kb[k] = __builtin_nontemporal_load((const u32x4 *)(kr + 64 + 8 * c));
+        va[k] = __builtin_nontemporal_load((const u32x4 *)(vr + 8 * c));
+        vb[k] = __builtin_nontemporal_load((const u32x4 *)(vr + 64 + 8 * c));
+      }
+    }
+    float sc[G][4];
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+#pragma unroll
+      for (int hh = 0; hh < G; hh++) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; e++) d = fdot2_bf16(ka[k][e], qa[hh][e], d);
+#pragma unroll
+        for (int e = 0; e < 4; e++) d = fdot2_bf16(kb[k][e], qb[hh][e], d);
+        d = sum8(d);
+        sc[hh][k] = ok[k] ? d * cs : -INFINITY;
+      }
+    float pk[G][4];
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) {
+      float mb = fmaxf(fmaxf(sc[hh][0], sc[hh][1]), fmaxf(sc[hh][2], sc[hh][3]));
+      mb = max_over_groups8(mb);  // row r0 is valid, so mb is finite
+      const float mn = fmaxf(m[hh], mb);
+      if (mn > m[hh]) {
+        const float alpha = exp2f(m[hh] - mn);  // 0 on the first step
+        l[hh] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; e++) acc[hh][e] *= alpha;
+        m[hh] = mn;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        pk[hh][k] = exp2f(sc[hh][k] - mn);
+        l[hh] += pk[hh][k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      float vf[16];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        vf[2 * e] = bf16lo(va[k][e]);
+        vf[2 * e + 1] = bf16hi(va[k][e]);
+        vf[8 + 2 * e] = bf16lo(vb[k][e]);
+        vf[8 + 2 * e + 1] = bf16hi(vb[k][e]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; hh++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) acc[hh][e] = __builtin_fmaf(pk[hh][k], vf[e], acc[hh][e]);
+    }
+  }
+
+  // combine the 8 lane groups of the wave (they share m), then the waves
+#pragma unroll
+  for (int hh = 0; hh < G; hh++) {
+    l[hh] = sum_over_groups8(l[hh]);
+#pragma unroll
+    for (int e = 0; e < 16; e++) acc[hh][e] = sum_over_groups8(acc[hh][e]);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        sm_acc[wave][hh][8 * c + e] = acc[hh][e];
+        sm_acc[wave][hh][64 + 8 * c + e] = acc[hh][8 + e];
+      }
+      if (c == 0) {
+        sm_m[wave][hh] = m[hh];
+        sm_l[wave][hh] = l[hh];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < G * kD; idx += kThreads) {
+    const int hh = idx / kD, d = idx % kD;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) mx = fmaxf(mx, sm_m[w][hh]);
+    float ls = 0.f, os = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; w++) {
+        const float f = exp2f(sm_m[w][hh] - mx);
+        ls += sm_l[w][hh] * f;
+        os += sm_acc[w][hh][d] * f;
+      }
+    }
+    const int h = g * G + hh;
+    if (splits == 1) {
+      ((uint16_t *)p.out)[((size_t)b * hq + h) * kD + d] = (uint16_t)pack_bf16(os / ls, 0.f);
+    } else {
+      const size_t slot = ((size_t)b * hq + h) * splits + sp;
+      p.ws_acc[slot * kD + d] = os;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = mx;
+        p.ws_ml[slot * 2 + 1] = ls;
+      }
+    }
+  }
+}
+
+// Merge the per-split partials of each (sequence, query head).
+__global__ __launch_bounds__(kD) void decode_combine_bf16_kernel(DecodeParams p) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const int S = p.splits;
+  const float *ml = p.ws_ml + (size_t)bh * S * 2;
+  const float *acc = p.ws_acc + (size_t)bh * S * kD;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; s++) mx = fmaxf(mx, ml[2 * s]);
+  float ls = 0.f, os = 0.f;
+  for (int s = 0; s < S; s++) {
+    const float ms = ml[2 * s];
+    if (ms == -INFINITY) continue;  // empty split
+    const float f = exp2f(ms - mx);
+    ls += ml[2 * s + 1] * f;
+    os += acc[(size_t)s * kD + d] * f;
+  }
+  ((uint16_t *)p.out)[(size_t)bh * kD + d] = (uint16_t)pack_bf16(os / ls, 0.f);
+}
+
+template <int G>
+hipError_t launch_g(const DecodeParams &p, hipStream_t stream) {
+  const unsigned n_wg = (unsigned)p.seq.num_seqs * p.cache.n_kv_heads * p.splits;
+  hipLaunchKernelGGL(decode_bf16_kernel<G>, dim3(n_wg), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(decode_combine_bf16_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads), dim3(kD), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeParams &p, int group, hipStream_t stream) {
+  if (p.seq.num_seqs == 0) return hipSuccess;
+  switch (group) {
+    case 1: return launch_g<1>(p, stream);
+    case 2: return launch_g<2>(p, stream);
+    case 4: return launch_g<4>(p, stream);
+    case 8: return launch_g<8>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swa

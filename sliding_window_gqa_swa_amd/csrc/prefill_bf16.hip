@@ -1,0 +1,296 @@
+// Chunked sliding-window GQA prefill, bf16 in / bf16 out, fp32 accumulation, gfx950.
+//
+// What it computes (Mistral 7B (Chinese translation), section 2):
+//   paragraph "Sliding Window Attention" / Figure 1 caption -- the query at
+//   absolute position i attends to keys j with i-W < j <= i;
+//   paragraph "Pre-fill and Chunking" / Figure 3 caption -- a chunk attends
+//   causally to itself and through the window to the cache; keys j below the
+//   chunk start come from ring slot j mod W (paragraph "Rolling Buffer Cache"),
+//   keys inside the chunk from the chunk's own k_new / v_new;
+//   section 1 -- grouped-query attention: the G query heads of KV head g share
+//   its keys and values.
+//
+// Design (MI355X / CDNA4):
+//   * One workgroup = (sequence, KV head g, tile of BQ query positions) x the G
+//     query heads of g: 8 waves, 32 query rows each, 256 rows per workgroup.
+//     Every K/V tile is staged ONCE in LDS and consumed by all G heads.
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16.  The S^T
+//     accumulator layout (lane = query, registers = keys) is reused directly
+//     as the B operand of the PV product, so P never leaves registers; V^T is
+//     read with ds_read_b64_tr_b16 (4-key transposed loads).
+//   * K/V tiles are BN = 64 keys aligned to multiples of 64 in absolute
+//     position.  Only the tiles intersecting the workgroup's band
+//     [q0-W+1, q_last] are visited; tiles wholly inside every row's band run
+//     without a mask.  Keys outside the band are zero-filled in LDS, never
+//     loaded, so unwritten cache slots cannot reach the arithmetic.
+//   * LDS rows are 256 B with a 16-byte-chunk XOR swizzle (chunk ^ row%16):
+//     conflict-free for the b128 K reads and the transposed V reads.
+//     K and V are double-buffered (64 KiB), one barrier per tile.
+//   * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
+//   * Workgroups are ordered heaviest-first and mapped XCD-contiguously.
+#include "device_common.h"
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBN = 64;                       // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = kD * 2;             // 256
+constexpr int kTileBytes = kBN * kRowBytes;   // 16 KiB
+constexpr int kLdsBytes = 4 * kTileBytes;     // K and V, double-buffered
+
+__device__ __forceinline__ int swz(int r, int chunk) { return r * kRowBytes + ((chunk ^ (r & 15)) << 4); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p) {
+  constexpr int kWph = kWaves / G;  // waves per query head
+  constexpr int kBQ = 32 * kWph;    // query positions per workgroup
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int work = xcd_logical_id(blockIdx.x, p.n_work);
+  const int tps = p.tiles_per_seq;
+  const int qt = tps - 1 - (work % tps);  // heaviest (latest) query tile first
+  const int bg = work / tps;
+  const int hkv = p.cache.n_kv_heads;
+  const int g = bg % hkv, b = bg / hkv;
+
+  const int tok0 = p.seq.cu_seqlens[b];
+  const int n_new = p.seq.cu_seqlens[b + 1] - tok0;
+  if (qt * kBQ >= n_new) return;
+  const int s = p.seq.start_pos[b];
+  const int crow = p.seq.cache_idx ? p.seq.cache_idx[b] : b;
+  const int W = p.cache.window;
+  const int q0 = s + qt * kBQ;
+  const int q_end = s + n_new;                    // one past the last query position
+  const int hi = min(q0 + kBQ, q_end) - 1;        // last key any row needs
+  const int lo = max(0, q0 - W + 1);              // first key any row needs
+  const int kt0 = (lo / kBN) * kBN;
+  const int n_tiles = (hi - kt0) / kBN + 1;
+  const int nomask_lo = q0 + kBQ - W;             // tiles in [nomask_lo, q0] need no mask
+
+  const int h = g * G + wave / kWph;
+  const int qbase = q0 + (wave % kWph) * 32;      // first query position of this wave
+  const int hq = p.n_q_heads;
+  const float c = p.scale_log2;
+
+  // ---- Q^T as MFMA B operand: lane -> query (lane & 15) of block qb, d-group (lane >> 4)
+  const uint16_t *Q = (const uint16_t *)p.q;
+  bf16x8 qf[4][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    const int qpos = qbase + 16 * qb + (lane & 15);
+    const bool ok = qpos < q_end;
+    const uint16_t *qrow = Q + ((size_t)(tok0 + qpos - s) * hq + h) * kD + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      u32x4 v = {0, 0, 0, 0};
+      if (ok) v = *(const u32x4 *)(qrow + 32 * ks);
+      qf[ks][qb] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- K/V tile staging: thread -> rows r0, r0 + 32, 16-byte chunk cc
+  const int r0 = tid >> 4, cc = tid & 15;
+  const uint16_t *ck = (const uint16_t *)p.cache.k, *cv = (const uint16_t *)p.cache.v;
+  const uint16_t *kn = (const uint16_t *)p.k_new, *vn = (const uint16_t *)p.v_new;
+  const size_t ring_row0 = ((size_t)crow * hkv + g) * (size_t)W;
+  u32x4 stg[4];
+  auto load_tile = [&](int ts) {
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int j = ts + r0 + 32 * u;
+      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (j >= lo && j <= hi) {
+        if (j < s) {
+          const size_t off = (ring_row0 + (size_t)(j % W)) * kD + cc * 8;
+          kv = *(const u32x4 *)(ck + off);
+          vv = *(const u32x4 *)(cv + off);
+        } else {
+          const size_t off = ((size_t)(tok0 + j - s) * hkv + g) * kD + cc * 8;
+          kv = *(const u32x4 *)(kn + off);
+          vv = *(const u32x4 *)(vn + off);
+        }
+      }
+      stg[u] = kv;
+      stg[2 + u] = vv;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char *kb = smem + buf * 2 * kTileBytes;
+    unsigned char *vb = kb + kTileBytes;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int off = swz(r0 + 32 * u, cc);
+      *(u32x4 *)(kb + off) = stg[u];
+      *(u32x4 *)(vb + off) = stg[2 + u];
+    }
+  };
+
+  f32x4 o[8][2];
+#pragma unroll
+  for (int db = 0; db < 8; db++)
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+
+  load_tile(kt0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; t++) {
+    const int ts = kt0 + t * kBN;
+    const bool has_next = t + 1 < n_tiles;
+    if (has_next) load_tile(ts + kBN);
+    const unsigned char *kb = smem + (t & 1) * 2 * kTileBytes;
+    const unsigned char *vb = kb + kTileBytes;
+
+    // S^T[key][query] for 4 key blocks of 16 x 2 query blocks of 16
+    f32x4 sa[4][2];
+#pragma unroll
+    for (int kbi = 0; kbi < 4; kbi++)
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+#pragma unroll
+      for (int kbi = 0; kbi < 4; kbi++) {
+        const int r = 16 * kbi + (lane & 15);
+        const bf16x8 kf = *(const bf16x8 *)(kb + swz(r, 4 * ks + (lane >> 4)));
+        sa[kbi][0] = mfma16(kf, qf[ks][0], sa[kbi][0]);
+        sa[kbi][1] = mfma16(kf, qf[ks][1], sa[kbi][1]);
+      }
+    }
+
+    // band mask on the tiles that cross a row's window edge or the diagonal
+    if (!(ts >= nomask_lo && ts + kBN - 1 <= q0)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) {
+        const int qpos = qbase + 16 * qb + (lane & 15);
+#pragma unroll
+        for (int kbi = 0; kbi < 4; kbi++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int key = ts + 16 * kbi + 4 * (lane >> 4) + i;
+            if (key > qpos || key <= qpos - W) sa[kbi][qb][i] = -INFINITY;
+          }
+      }
+    }
+
+    // online softmax (per query; a query's 64 keys sit in lanes l, l^16, l^32, l^48)
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kbi = 0; kbi < 4; kbi++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) mt = fmaxf(mt, sa[kbi][qb][i]);
+      mt = fmaxf(mt, xor16(mt));
+      mt = fmaxf(mt, xor32(mt));
+      const float mn = fmaxf(m[qb], mt);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = (m[qb] == -INFINITY) ? 0.f : exp2f((m[qb] - mu) * c);
+      const float mc = mu * c;
+      m[qb] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int kbi = 0; kbi < 4; kbi++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float pv = exp2f(__builtin_fmaf(sa[kbi][qb][i], c, -mc));
+          sa[kbi][qb][i] = pv;
+          ls += pv;
+        }
+      l[qb] = l[qb] * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
+    }
+
+    // O^T += V^T P^T over two 32-key slices
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; qb++) {
+        u32x4 w;
+        w[0] = pack_bf16(sa[2 * kk][qb][0], sa[2 * kk][qb][1]);
+        w[1] = pack_bf16(sa[2 * kk][qb][2], sa[2 * kk][qb][3]);
+        w[2] = pack_bf16(sa[2 * kk + 1][qb][0], sa[2 * kk + 1][qb][1]);
+        w[3] = pack_bf16(sa[2 * kk + 1][qb][2], sa[2 * kk + 1][qb][3]);
+        pf[qb] = __builtin_bit_cast(bf16x8, w);
+      }
+      const int r1 = 32 * kk + 4 * (lane >> 4) + ((lane & 15) >> 2);
+#pragma unroll
+      for (int db = 0; db < 8; db++) {
+        const int dcol = 16 * db + 4 * (lane & 3);
+        const int o1 = swz(r1, dcol >> 3) + ((dcol & 7) << 1);
+        const int o2 = swz(r1 + 16, dcol >> 3) + ((dcol & 7) << 1);
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + o1));
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + o2));
+        u32x4 w;
+        w[0] = __builtin_bit_cast(u32x2, v1)[0];
+        w[1] = __builtin_bit_cast(u32x2, v1)[1];
+        w[2] = __builtin_bit_cast(u32x2, v2)[0];
+        w[3] = __builtin_bit_cast(u32x2, v2)[1];
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+        o[db][0] = mfma16(vf, pf[0], o[db][0]);
+        o[db][1] = mfma16(vf, pf[1], o[db][1]);
+      }
+    }
+
+    if (has_next) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // epilogue: finish the row sums across the 4 lane groups, normalise, store bf16
+  uint16_t *O = (uint16_t *)p.out;
+#pragma unroll
+  for (int qb = 0; qb < 2; qb++) {
+    float lt = l[qb];
+    lt += xor16(lt);
+    lt += xor32(lt);
+    const float inv = 1.0f / lt;
+    const int qpos = qbase + 16 * qb + (lane & 15);
+    if (qpos < q_end) {
+      uint16_t *orow = O + ((size_t)(tok0 + qpos - s) * hq + h) * kD + 4 * (lane >> 4);
+#pragma unroll
+      for (int db = 0; db < 8; db++) {
+        u32x2 w;
+        w[0] = pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv);
+        w[1] = pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv);
+        *(u32x2 *)(orow + 16 * db) = w;
+      }
+    }
+  }
+}
+
+template <int G>
+hipError_t launch_g(const PrefillParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_bf16_kernel<G>, dim3((unsigned)p.n_work), dim3(kThreads), kLdsBytes, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_bf16_tile_rows(int group) { return 32 * (kWaves / group); }
+
+hipError_t launch_prefill_bf16(const PrefillParams &p, int group, hipStream_t stream) {
+  if (p.n_work == 0) return hipSuccess;
+  switch (group) {
+    case 1: return launch_g<1>(p, stream);
+    case 2: return launch_g<2>(p, stream);
+    case 4: return launch_g<4>(p, stream);
+    case 8: return launch_g<8>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swa

@@ -1,0 +1,84 @@
+// Launch parameters and launchers shared between the C-ABI layer (api.hip) and
+// the kernels.  Plain structs passed by value to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+// Metadata of the sequences of one call (device pointers).
+struct SeqMeta {
+  const int32_t *cu_seqlens;  // [num_seqs + 1]; NULL in decode (token b = sequence b)
+  const int32_t *start_pos;   // [num_seqs]
+  const int32_t *cache_idx;   // [num_seqs] or NULL (row b)
+  int32_t num_seqs;
+  int32_t max_new_tokens;
+};
+
+struct CacheRef {
+  const void *k;
+  const void *v;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t window;
+  int32_t elt_bytes;
+};
+
+struct CacheWriteParams {
+  SeqMeta seq;
+  void *cache_k;
+  void *cache_v;
+  const void *k_new;
+  const void *v_new;
+  int32_t n_kv_heads;
+  int32_t window;
+  int32_t row_chunks;  // 16-byte chunks per row (head_dim * elt / 16)
+};
+
+struct PrefillParams {
+  SeqMeta seq;
+  CacheRef cache;
+  const void *q;
+  const void *k_new;
+  const void *v_new;
+  void *out;
+  int32_t n_q_heads;
+  int32_t tiles_per_seq;  // query tiles per sequence (ceil(max_new_tokens / tile))
+  int32_t n_work;         // num_seqs * tiles_per_seq * n_kv_heads
+  float scale_log2;       // sm_scale * log2(e)
+  float sm_scale;
+};
+
+struct DecodeParams {
+  SeqMeta seq;
+  CacheRef cache;
+  const void *q;
+  void *out;
+  float *ws_acc;  // [num_seqs][n_q_heads][splits][head_dim]
+  float *ws_ml;   // [num_seqs][n_q_heads][splits][2]  (max in log2 units, sum)
+  int32_t n_q_heads;
+  int32_t splits;
+  int32_t split_len;  // slots per split
+  float scale_log2;
+  float sm_scale;
+};
+
+// Decode plan: how the window of each (sequence, KV head) is split across workgroups.
+struct DecodePlan {
+  int32_t splits;
+  int32_t split_len;
+  size_t workspace_bytes;
+};
+DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, int32_t head_dim,
+                       int32_t window, int32_t dtype);
+
+hipError_t launch_cache_write(const CacheWriteParams &p, hipStream_t stream);
+int prefill_bf16_tile_rows(int group);
+hipError_t launch_prefill_bf16(const PrefillParams &p, int group, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams &p, int group, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream);
+
+}  // namespace swa
