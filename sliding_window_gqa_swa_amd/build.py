@@ -31,6 +31,11 @@ def hipcc() -> str:
 def compile_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # NaN operands are not given special treatment by min/max (no extra
+            # canonicalising instructions); infinities keep their IEEE meaning,
+            # which the masking relies on.  NaNs in the inputs still propagate
+            # through the arithmetic to the outputs.
+            "-fno-honor-nans", "-mno-amdgpu-ieee",
             "-I", CSRC]
 
 

@@ -23,9 +23,10 @@
 //     [q0-W+1, q_last] are visited; tiles wholly inside every row's band run
 //     without a mask.  Keys outside the band are zero-filled in LDS, never
 //     loaded, so unwritten cache slots cannot reach the arithmetic.
-//   * LDS rows are 256 B with a 16-byte-chunk XOR swizzle (chunk ^ row%16):
-//     conflict-free for the b128 K reads and the transposed V reads.
-//     K and V are double-buffered (64 KiB), one barrier per tile.
+//   * LDS rows are 256 B of data padded to 272 B: consecutive rows start 4 banks
+//     apart, so the b128 K reads and the transposed V reads spread over all
+//     banks, and every operand address is a per-lane base plus an immediate.
+//     K and V are double-buffered (68 KiB), one barrier per tile.
 //   * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
 //   * Workgroups are ordered heaviest-first and mapped XCD-contiguously.
 #include "device_common.h"
@@ -38,11 +39,12 @@ constexpr int kD = 128;
 constexpr int kBN = 64;                       // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowBytes = kD * 2;             // 256
-constexpr int kTileBytes = kBN * kRowBytes;   // 16 KiB
+constexpr int kRowBytes = kD * 2 + 16;        // 256 B of data + 16 B of padding
+constexpr int kTileBytes = kBN * kRowBytes;   // 17 KiB
 constexpr int kLdsBytes = 4 * kTileBytes;     // K and V, double-buffered
+constexpr float kRescaleSlack = 8.0f;         // log2 units: weights stay <= 256
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 
-__device__ __forceinline__ int swz(int r, int chunk) { return r * kRowBytes + ((chunk ^ (r & 15)) << 4); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -55,18 +57,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int work = xcd_logical_id(blockIdx.x, p.n_work);
+  const int work = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, p.n_work));
   const int tps = p.tiles_per_seq;
   const int qt = tps - 1 - (work % tps);  // heaviest (latest) query tile first
   const int bg = work / tps;
   const int hkv = p.cache.n_kv_heads;
-  const int g = bg % hkv, b = bg / hkv;
+  const int g = __builtin_amdgcn_readfirstlane(bg % hkv), b = __builtin_amdgcn_readfirstlane(bg / hkv);
 
-  const int tok0 = p.seq.cu_seqlens[b];
-  const int n_new = p.seq.cu_seqlens[b + 1] - tok0;
+  // workgroup-uniform metadata (kept in scalar registers)
+  const int tok0 = __builtin_amdgcn_readfirstlane(p.seq.cu_seqlens[b]);
+  const int n_new = __builtin_amdgcn_readfirstlane(p.seq.cu_seqlens[b + 1]) - tok0;
   if (qt * kBQ >= n_new) return;
-  const int s = p.seq.start_pos[b];
-  const int crow = p.seq.cache_idx ? p.seq.cache_idx[b] : b;
+  const int s = __builtin_amdgcn_readfirstlane(p.seq.start_pos[b]);
+  const int crow = p.seq.cache_idx ? __builtin_amdgcn_readfirstlane(p.seq.cache_idx[b]) : b;
   const int W = p.cache.window;
   const int q0 = s + qt * kBQ;
   const int q_end = s + n_new;                    // one past the last query position
@@ -97,11 +100,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     }
   }
 
-  // ---- K/V tile staging: thread -> rows r0, r0 + 32, 16-byte chunk cc
+  // ---- K/V tile staging: thread -> rows r0, r0 + 32 of a tile, 16-byte chunk cc.
+  // Keys below the chunk start come from ring slot j mod W (advanced
+  // incrementally by 64 per tile), keys from the chunk on from k_new / v_new.
   const int r0 = tid >> 4, cc = tid & 15;
   const uint16_t *ck = (const uint16_t *)p.cache.k, *cv = (const uint16_t *)p.cache.v;
   const uint16_t *kn = (const uint16_t *)p.k_new, *vn = (const uint16_t *)p.v_new;
-  const size_t ring_row0 = ((size_t)crow * hkv + g) * (size_t)W;
+  const int64_t ring_base = ((int64_t)crow * hkv + g) * (int64_t)W * kD + cc * 8;
+  const int64_t new_stride = (int64_t)hkv * kD;
+  const int64_t new_base = ((int64_t)(tok0 - s) * hkv + g) * kD + cc * 8;  // + j * new_stride
+  const int slot_step = kBN % W;
+  int slot[2] = {(kt0 + r0) % W, (kt0 + r0 + 32) % W};
   u32x4 stg[4];
   auto load_tile = [&](int ts) {
 #pragma unroll
@@ -109,51 +118,46 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       const int j = ts + r0 + 32 * u;
       u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
       if (j >= lo && j <= hi) {
-        if (j < s) {
-          const size_t off = (ring_row0 + (size_t)(j % W)) * kD + cc * 8;
-          kv = *(const u32x4 *)(ck + off);
-          vv = *(const u32x4 *)(cv + off);
-        } else {
-          const size_t off = ((size_t)(tok0 + j - s) * hkv + g) * kD + cc * 8;
-          kv = *(const u32x4 *)(kn + off);
-          vv = *(const u32x4 *)(vn + off);
-        }
+        const bool ring = j < s;
+        const int64_t off = ring ? ring_base + (int64_t)slot[u] * kD : new_base + (int64_t)j * new_stride;
+        const uint16_t *kp = ring ? ck : kn;
+        const uint16_t *vp = ring ? cv : vn;
+        kv = *(const u32x4 *)(kp + off);
+        vv = *(const u32x4 *)(vp + off);
       }
       stg[u] = kv;
       stg[2 + u] = vv;
+      slot[u] += slot_step;
+      if (slot[u] >= W) slot[u] -= W;
     }
   };
+  const int st_off0 = r0 * kRowBytes + cc * 16, st_off1 = st_off0 + 32 * kRowBytes;
   auto store_tile = [&](int buf) {
     unsigned char *kb = smem + buf * 2 * kTileBytes;
     unsigned char *vb = kb + kTileBytes;
-#pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int off = swz(r0 + 32 * u, cc);
-      *(u32x4 *)(kb + off) = stg[u];
-      *(u32x4 *)(vb + off) = stg[2 + u];
-    }
+    *(u32x4 *)(kb + st_off0) = stg[0];
+    *(u32x4 *)(kb + st_off1) = stg[1];
+    *(u32x4 *)(vb + st_off0) = stg[2];
+    *(u32x4 *)(vb + st_off1) = stg[3];
   };
+  // LDS byte offsets of this lane's MFMA operand reads.  With padded rows every
+  // read is this per-lane base plus a compile-time constant.
+  //   K (A operand of S^T): row 16*kbi + lane%16, columns 32*ks + 8*(lane/16) .. +8
+  //   V (transposed reads): rows 32*kk + 4*(lane/16) + (lane%16)/4 (+16),
+  //                         columns 16*db + 4*(lane%4) .. +4
+  const int k_lane = (lane & 15) * kRowBytes + (lane >> 4) * 16;
+  const int v_lane = (4 * (lane >> 4) + ((lane & 15) >> 2)) * kRowBytes + 8 * (lane & 3);
 
   f32x4 o[8][2];
 #pragma unroll
   for (int db = 0; db < 8; db++)
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};  // running max, log2 units
+  float l[2] = {0.f, 0.f};              // this lane's share of the row sums
 
-  load_tile(kt0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; t++) {
-    const int ts = kt0 + t * kBN;
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) load_tile(ts + kBN);
-    const unsigned char *kb = smem + (t & 1) * 2 * kTileBytes;
-    const unsigned char *vb = kb + kTileBytes;
-
-    // S^T[key][query] for 4 key blocks of 16 x 2 query blocks of 16
+  // One K/V tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+  auto tile = [&](const unsigned char *kb, const unsigned char *vb, int ts, bool masked) {
     f32x4 sa[4][2];
 #pragma unroll
     for (int kbi = 0; kbi < 4; kbi++)
@@ -163,57 +167,52 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++) {
-        const int r = 16 * kbi + (lane & 15);
-        const bf16x8 kf = *(const bf16x8 *)(kb + swz(r, 4 * ks + (lane >> 4)));
+        const bf16x8 kf = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kRowBytes + 64 * ks);
         sa[kbi][0] = mfma16(kf, qf[ks][0], sa[kbi][0]);
         sa[kbi][1] = mfma16(kf, qf[ks][1], sa[kbi][1]);
       }
     }
-
-    // band mask on the tiles that cross a row's window edge or the diagonal
-    if (!(ts >= nomask_lo && ts + kBN - 1 <= q0)) {
+    if (masked) {
+      // key - query for this lane's first element; valid iff -W < key - query <= 0
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) {
-        const int qpos = qbase + 16 * qb + (lane & 15);
+        const int d0 = ts + 4 * (lane >> 4) - (qbase + 16 * qb + (lane & 15)) + W - 1;
 #pragma unroll
         for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int key = ts + 16 * kbi + 4 * (lane >> 4) + i;
-            if (key > qpos || key <= qpos - W) sa[kbi][qb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 4; i++)
+            if ((unsigned)(d0 + 16 * kbi + i) >= (unsigned)W) sa[kbi][qb][i] = -INFINITY;
       }
     }
-
-    // online softmax (per query; a query's 64 keys sit in lanes l, l^16, l^32, l^48)
+    // Online softmax per query; a query's 64 keys sit in lanes l, l^16, l^32, l^48.
+    // The running max m is kept in log2 units (score * scale * log2 e) and only
+    // moves when a tile's max exceeds it by more than kRescaleSlack: the
+    // weights then stay <= 2^kRescaleSlack, the O/l rescale runs only on those
+    // (rare) tiles, and the result is unchanged because O and l share m.
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
       float mt = -INFINITY;
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) mt = fmaxf(mt, sa[kbi][qb][i]);
+        mt = fmaxf(mt, fmaxf(fmaxf(sa[kbi][qb][0], sa[kbi][qb][1]), fmaxf(sa[kbi][qb][2], sa[kbi][qb][3])));
       mt = fmaxf(mt, xor16(mt));
       mt = fmaxf(mt, xor32(mt));
-      const float mn = fmaxf(m[qb], mt);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = (m[qb] == -INFINITY) ? 0.f : exp2f((m[qb] - mu) * c);
-      const float mc = mu * c;
-      m[qb] = mn;
-      float ls = 0.f;
+      const float mts = mt * c;
+      const bool upd = mts > m[qb] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        const float mn = upd ? mts : m[qb];
+        const float alpha = (m[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[qb] - mn);
+        m[qb] = mn;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
+      }
+      const float mc = (m[qb] == -INFINITY) ? 0.f : m[qb];
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const float pv = exp2f(__builtin_fmaf(sa[kbi][qb][i], c, -mc));
-          sa[kbi][qb][i] = pv;
-          ls += pv;
-        }
-      l[qb] = l[qb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
+        for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kbi][qb][i], c, -mc));
     }
-
     // O^T += V^T P^T over two 32-key slices
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) {
@@ -226,15 +225,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         w[2] = pack_bf16(sa[2 * kk + 1][qb][0], sa[2 * kk + 1][qb][1]);
         w[3] = pack_bf16(sa[2 * kk + 1][qb][2], sa[2 * kk + 1][qb][3]);
         pf[qb] = __builtin_bit_cast(bf16x8, w);
+        // row sum of the bf16-rounded weights, i.e. of exactly what enters P V
+#pragma unroll
+        for (int e = 0; e < 4; e++) l[qb] = fdot2_bf16(w[e], kBf16OnePair, l[qb]);
       }
-      const int r1 = 32 * kk + 4 * (lane >> 4) + ((lane & 15) >> 2);
 #pragma unroll
       for (int db = 0; db < 8; db++) {
-        const int dcol = 16 * db + 4 * (lane & 3);
-        const int o1 = swz(r1, dcol >> 3) + ((dcol & 7) << 1);
-        const int o2 = swz(r1 + 16, dcol >> 3) + ((dcol & 7) << 1);
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + o1));
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + o2));
+        const unsigned char *va = vb + v_lane + 32 * kk * kRowBytes + 32 * db;
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowBytes));
         u32x4 w;
         w[0] = __builtin_bit_cast(u32x2, v1)[0];
         w[1] = __builtin_bit_cast(u32x2, v1)[1];
@@ -245,10 +244,32 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         o[db][1] = mfma16(vf, pf[1], o[db][1]);
       }
     }
+  };
 
+  // Tiles needing a mask form a prefix (window's lower edge) and a suffix (the
+  // diagonal) of the tile range; the interior runs the unmasked body.
+  //   unmasked  <=>  ts >= nomask_lo  and  ts + kBN - 1 <= q0
+  const int n_lead = min(n_tiles, max(0, (nomask_lo - kt0 + kBN - 1) / kBN));
+  const int n_diag_free = (q0 - kBN + 1 - kt0) >= 0 ? (q0 - kBN + 1 - kt0) / kBN + 1 : 0;
+  const int t_mid_end = max(n_lead, min(n_tiles, n_diag_free));
+
+  auto step = [&](int t, bool masked) {
+    const int ts = kt0 + t * kBN;
+    const bool has_next = t + 1 < n_tiles;
+    if (has_next) load_tile(ts + kBN);
+    const unsigned char *kb = smem + (t & 1) * 2 * kTileBytes;
+    tile(kb, kb + kTileBytes, ts, masked);
     if (has_next) store_tile((t + 1) & 1);
     __syncthreads();
-  }
+  };
+
+  load_tile(kt0);
+  store_tile(0);
+  __syncthreads();
+  int t = 0;
+  for (; t < n_lead; t++) step(t, true);
+  for (; t < t_mid_end; t++) step(t, false);
+  for (; t < n_tiles; t++) step(t, true);
 
   // epilogue: finish the row sums across the 4 lane groups, normalise, store bf16
   uint16_t *O = (uint16_t *)p.out;
