@@ -51,9 +51,21 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-// Value of lane (l ^ 16) / (l ^ 32).
-__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16); }
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// Value of lane (l ^ 16) / (l ^ 32), through the gfx950 row-swap instructions
+// (plain VALU, no LDS round trip).  permlane16_swap(x, x) returns x with rows
+// 1 and 3 replaced by rows 0 and 2, and x with rows 0 and 2 replaced by rows
+// 1 and 3 (a row is 16 lanes); lane l of the result that is not its own row
+// holds the value of lane l ^ 16.  Likewise for halves of 32 lanes.
+__device__ __forceinline__ float xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const int lane = __lane_id();
+  return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const int lane = __lane_id();
+  return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
 
 // Reductions over lanes {l, l^8, l^16, ...}: combine groups of 8 lanes.
 __device__ __forceinline__ float max_over_groups8(float x) {

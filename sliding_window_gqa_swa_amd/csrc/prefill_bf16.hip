@@ -23,10 +23,11 @@
 //     [q0-W+1, q_last] are visited; tiles wholly inside every row's band run
 //     without a mask.  Keys outside the band are zero-filled in LDS, never
 //     loaded, so unwritten cache slots cannot reach the arithmetic.
-//   * LDS rows are 256 B of data padded to 272 B: consecutive rows start 4 banks
-//     apart, so the b128 K reads and the transposed V reads spread over all
-//     banks, and every operand address is a per-lane base plus an immediate.
-//     K and V are double-buffered (68 KiB), one barrier per tile.
+//   * LDS rows are padded: K rows to 272 B (consecutive rows 4 banks apart: the
+//     16-byte K reads of 8 rows cover all 32 banks), V rows to 288 B (rows 8
+//     banks apart: the 4 rows x 32 B of a transposed read of 16 lanes hit
+//     disjoint banks).  Every operand address is a per-lane base plus an
+//     immediate.  K and V are double-buffered (70 KiB), one barrier per tile.
 //   * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
 //   * Workgroups are ordered heaviest-first and mapped XCD-contiguously.
 #include "device_common.h"
@@ -39,9 +40,12 @@ constexpr int kD = 128;
 constexpr int kBN = 64;                       // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowBytes = kD * 2 + 16;        // 256 B of data + 16 B of padding
-constexpr int kTileBytes = kBN * kRowBytes;   // 17 KiB
-constexpr int kLdsBytes = 4 * kTileBytes;     // K and V, double-buffered
+constexpr int kKRow = kD * 2 + 16;            // K rows: 256 B of data + 16 B of padding
+constexpr int kVRow = kD * 2 + 32;            // V rows: 256 B of data + 32 B of padding
+constexpr int kKTile = kBN * kKRow;
+constexpr int kVTile = kBN * kVRow;
+constexpr int kBufBytes = kKTile + kVTile;    // one K tile + one V tile
+constexpr int kLdsBytes = 2 * kBufBytes;      // double-buffered
 constexpr float kRescaleSlack = 8.0f;         // log2 units: weights stay <= 256
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 
@@ -131,22 +135,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       if (slot[u] >= W) slot[u] -= W;
     }
   };
-  const int st_off0 = r0 * kRowBytes + cc * 16, st_off1 = st_off0 + 32 * kRowBytes;
+  const int kst = r0 * kKRow + cc * 16, vst = r0 * kVRow + cc * 16;
   auto store_tile = [&](int buf) {
-    unsigned char *kb = smem + buf * 2 * kTileBytes;
-    unsigned char *vb = kb + kTileBytes;
-    *(u32x4 *)(kb + st_off0) = stg[0];
-    *(u32x4 *)(kb + st_off1) = stg[1];
-    *(u32x4 *)(vb + st_off0) = stg[2];
-    *(u32x4 *)(vb + st_off1) = stg[3];
+    unsigned char *kb = smem + buf * kBufBytes;
+    unsigned char *vb = kb + kKTile;
+    *(u32x4 *)(kb + kst) = stg[0];
+    *(u32x4 *)(kb + kst + 32 * kKRow) = stg[1];
+    *(u32x4 *)(vb + vst) = stg[2];
+    *(u32x4 *)(vb + vst + 32 * kVRow) = stg[3];
   };
   // LDS byte offsets of this lane's MFMA operand reads.  With padded rows every
   // read is this per-lane base plus a compile-time constant.
   //   K (A operand of S^T): row 16*kbi + lane%16, columns 32*ks + 8*(lane/16) .. +8
   //   V (transposed reads): rows 32*kk + 4*(lane/16) + (lane%16)/4 (+16),
   //                         columns 16*db + 4*(lane%4) .. +4
-  const int k_lane = (lane & 15) * kRowBytes + (lane >> 4) * 16;
-  const int v_lane = (4 * (lane >> 4) + ((lane & 15) >> 2)) * kRowBytes + 8 * (lane & 3);
+  const int k_lane = (lane & 15) * kKRow + (lane >> 4) * 16;
+  const int v_lane = (4 * (lane >> 4) + ((lane & 15) >> 2)) * kVRow + 8 * (lane & 3);
 
   f32x4 o[8][2];
 #pragma unroll
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++) {
-        const bf16x8 kf = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kRowBytes + 64 * ks);
+        const bf16x8 kf = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kKRow + 64 * ks);
         sa[kbi][0] = mfma16(kf, qf[ks][0], sa[kbi][0]);
         sa[kbi][1] = mfma16(kf, qf[ks][1], sa[kbi][1]);
       }
@@ -231,9 +235,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       }
 #pragma unroll
       for (int db = 0; db < 8; db++) {
-        const unsigned char *va = vb + v_lane + 32 * kk * kRowBytes + 32 * db;
+        const unsigned char *va = vb + v_lane + 32 * kk * kVRow + 32 * db;
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowBytes));
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kVRow));
         u32x4 w;
         w[0] = __builtin_bit_cast(u32x2, v1)[0];
         w[1] = __builtin_bit_cast(u32x2, v1)[1];
@@ -257,8 +261,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const int ts = kt0 + t * kBN;
     const bool has_next = t + 1 < n_tiles;
     if (has_next) load_tile(ts + kBN);
-    const unsigned char *kb = smem + (t & 1) * 2 * kTileBytes;
-    tile(kb, kb + kTileBytes, ts, masked);
+    const unsigned char *kb = smem + (t & 1) * kBufBytes;
+    tile(kb, kb + kKTile, ts, masked);
     if (has_next) store_tile((t + 1) & 1);
     __syncthreads();
   };
