@@ -74,8 +74,8 @@ def cpu_baseline(wl, sample_rows: int):
     dt = time.perf_counter() - t0
     flops = 4.0 * wl.head_dim * wl.n_q_heads * sum(min(int(i) + 1, wl.window) for i in rows)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{len(rows)} evenly spaced query rows x {wl.n_q_heads} heads of the 16384-token prefill "
-                      f"(W={wl.window}), fp64, {flops / 1e9:.1f} GFLOP in {dt:.2f} s"}
+            "sample": f"{len(rows)} of the {n} query rows (evenly spaced) x {wl.n_q_heads} heads of the "
+                      f"16384-token prefill (W={wl.window}), fp64, {flops / 1e9:.1f} GFLOP in {dt:.2f} s"}
 
 
 def main():
@@ -84,7 +84,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--cpu-sample-rows", type=int, default=16384)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
