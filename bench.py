@@ -78,6 +78,97 @@ def cpu_baseline(wl, sample_rows: int):
                       f"16384-token prefill (W={wl.window}), fp64, {flops / 1e9:.1f} GFLOP in {dt:.2f} s"}
 
 
+def time_ms(fn, reps: int) -> float:
+    """Mean milliseconds of `fn` over `reps` launches, HIP events on the current stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def suite(up, pq, pk, pv, pout, scale, reps: int):
+    """The other workloads of the path, timed (their parity is covered by the GPU tests)."""
+    import numpy as np
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    from sliding_window_gqa_swa_amd.workloads import chunked_sequences, ragged_mixed
+    dev = pq.device
+    res = {}
+    # causal attention = the same kernel with W >= N: the paper's "standard attention" at 16K
+    n = pq.shape[0]
+    cc = swa.Cache(torch.zeros((1, 8, n, 128), dtype=torch.bfloat16, device=dev),
+                   torch.zeros((1, 8, n, 128), dtype=torch.bfloat16, device=dev))
+    b1 = swa.Batch([n], [0], [0])
+    t_causal = time_ms(lambda: swa.swa_prefill_chunk(cc, b1, pq, 32, pk, pv, scale, pout), reps)
+    causal_flops = 4.0 * 128 * 32 * band_pairs(0, n, n)
+    res["causal_prefill_16k"] = {"ms": round(t_causal, 4), "tflops": round(causal_flops / t_causal / 1e9, 1)}
+    del cc
+
+    # chunked prefill through the ring: 4 x 32768 tokens in 8 chunks of 4096, W = 4096
+    B, N, C, W = 4, 32768, 4096, 4096
+    q, k, v = chunked_sequences(1003, batch=B, n=N, window=W)
+    qd, kd, vd = up(q), up(k), up(v)
+    del q, k, v
+    cache = swa.Cache(torch.zeros((B, 8, W, 128), dtype=torch.bfloat16, device=dev),
+                      torch.zeros((B, 8, W, 128), dtype=torch.bfloat16, device=dev))
+    oc = torch.empty((B * C, 32, 128), dtype=torch.bfloat16, device=dev)
+    chunks = []
+    for s in range(0, N, C):
+        batch = swa.Batch([C] * B, [s] * B, list(range(B)))
+        qc = qd[:, s:s + C].reshape(B * C, 32, 128).contiguous()
+        kc = kd[:, s:s + C].reshape(B * C, 8, 128).contiguous()
+        vc = vd[:, s:s + C].reshape(B * C, 8, 128).contiguous()
+        t_p = time_ms(lambda: swa.swa_prefill_chunk(cache, batch, qc, 32, kc, vc, scale, oc), reps)
+        t_w = time_ms(lambda: swa.swa_cache_write(cache, batch, kc, vc), reps)
+        fl = 4.0 * 128 * 32 * B * band_pairs(s, C, W)
+        chunks.append((t_p, t_w, fl))
+    del qd, kd, vd
+    tot_ms = sum(c[0] for c in chunks)
+    tot_fl = sum(c[2] for c in chunks)
+    wbytes = 2 * 2 * B * C * 8 * 128 * 2
+    res["chunked_4x32k_w4096"] = {
+        "prefill_ms_per_chunk": [round(c[0], 4) for c in chunks],
+        "prefill_tflops_chunks_1_7": round(sum(c[2] for c in chunks[1:]) / sum(c[0] for c in chunks[1:]) / 1e9, 1),
+        "prefill_tflops_all": round(tot_fl / tot_ms / 1e9, 1),
+        "cache_write_ms_per_chunk": round(float(np.mean([c[1] for c in chunks])), 4),
+        "cache_write_gbps": round(wbytes / float(np.mean([c[1] for c in chunks])) / 1e6, 1)}
+    del cache
+
+    # ragged mixed batch: 16 prefill + 32 decode sequences sharing one 48-row cache
+    for variant in (False, True):
+        wp, wd = ragged_mixed(1005, variant=variant)
+        cache = swa.Cache(torch.zeros((48, 8, W, 128), dtype=torch.bfloat16, device=dev),
+                          torch.zeros((48, 8, W, 128), dtype=torch.bfloat16, device=dev))
+        for wl in (wp, wd):
+            hb = swa.Batch([s.start_pos - s.hist_lo for s in wl.seqs], [s.hist_lo for s in wl.seqs], wl.cache_idx)
+            swa.swa_cache_write(cache, hb, up(wl.hist_packed("k")), up(wl.hist_packed("v")))
+        pb = swa.Batch([s.n_new for s in wp.seqs], [s.start_pos for s in wp.seqs], wp.cache_idx)
+        mq, mk, mv = up(wp.q), up(wp.k_new), up(wp.v_new)
+        mo = torch.empty((wp.total_tokens, 32, 128), dtype=torch.bfloat16, device=dev)
+        db = swa.Batch([1] * wd.num_seqs, [s.start_pos for s in wd.seqs], wd.cache_idx)
+        dq, dk, dv = up(wd.q), up(wd.k_new), up(wd.v_new)
+        do = torch.empty((wd.num_seqs, 32, 128), dtype=torch.bfloat16, device=dev)
+        wsb = swa.swa_decode_workspace_size(cache, wd.num_seqs, 32)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        t_p = time_ms(lambda: swa.swa_prefill_chunk(cache, pb, mq, 32, mk, mv, scale, mo), reps)
+        t_dw = time_ms(lambda: swa.swa_cache_write(cache, db, dk, dv), reps)
+        t_d = time_ms(lambda: swa.swa_decode(cache, db, dq, 32, scale, do, ws, wsb), reps)
+        pfl = 4.0 * 128 * 32 * sum(band_pairs(s.start_pos, s.n_new, W) for s in wp.seqs)
+        kvb = sum(2 * 8 * 128 * 2 * min(s.start_pos + 1, W) for s in wd.seqs)
+        res["mixed_" + ("ctx8192" if variant else "loguniform")] = {
+            "prefill_ms": round(t_p, 4), "prefill_tflops": round(pfl / t_p / 1e9, 1),
+            "decode_us": round(t_d * 1e3, 1), "decode_gbps": round(kvb / t_d / 1e6, 1),
+            "decode_write_us": round(t_dw * 1e3, 1)}
+        del cache
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +176,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
+    ap.add_argument("--no-suite", action="store_true", help="skip the chunked / mixed / causal workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -205,6 +297,10 @@ def main():
         "pages_context": {"swa_vs_standard_speedup_at_16k_w4096": 2.0, "cache_memory_reduction_at_32k": 8.0,
                           "hardware": "not stated"},
     }
+    if not args.no_suite:
+        result["suite"] = suite(up, pq, pk, pv, pout, wp.scale, reps=10)
+        result["suite"]["swa_vs_causal_speedup_16k"] = round(
+            result["suite"]["causal_prefill_16k"]["ms"] / t_pre, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wp, args.cpu_sample_rows)
     print(json.dumps(result))
