@@ -161,21 +161,34 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   float l[2] = {0.f, 0.f};              // this lane's share of the row sums
 
   // One K/V tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
-  auto tile = [&](const unsigned char *kb, const unsigned char *vb, int ts, bool masked) {
+  auto tile = [&](const unsigned char *kb, const unsigned char *vb, int ts, bool masked, bool has_next) {
     f32x4 sa[4][2];
 #pragma unroll
     for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments are read one 32-wide d-step ahead of the MFMAs that use them,
+    // so the LDS latency overlaps the matrix work of the previous step.
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int kbi = 0; kbi < 4; kbi++) kf[0][kbi] = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kKRow);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int kbi = 0; kbi < 4; kbi++)
+          kf[(ks + 1) & 1][kbi] = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kKRow + 64 * (ks + 1));
+      }
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++) {
-        const bf16x8 kf = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kKRow + 64 * ks);
-        sa[kbi][0] = mfma16(kf, qf[ks][0], sa[kbi][0]);
-        sa[kbi][1] = mfma16(kf, qf[ks][1], sa[kbi][1]);
+        sa[kbi][0] = mfma16(kf[ks & 1][kbi], qf[ks][0], sa[kbi][0]);
+        sa[kbi][1] = mfma16(kf[ks & 1][kbi], qf[ks][1], sa[kbi][1]);
       }
     }
+    // the next tile's global loads are issued here, after the K fragments of
+    // this tile are consumed (shorter register live ranges); their latency is
+    // covered by the softmax and PV work below
+    if (has_next) load_tile(ts + kBN);
     if (masked) {
       // key - query for this lane's first element; valid iff -W < key - query <= 0
 #pragma unroll
@@ -233,8 +246,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
         for (int e = 0; e < 4; e++) l[qb] = fdot2_bf16(w[e], kBf16OnePair, l[qb]);
       }
-#pragma unroll
-      for (int db = 0; db < 8; db++) {
+      // V fragments are read one 16-column block ahead of their MFMAs.
+      auto vread = [&](int db) {
         const unsigned char *va = vb + v_lane + 32 * kk * kVRow + 32 * db;
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
         const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kVRow));
@@ -243,9 +256,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         w[1] = __builtin_bit_cast(u32x2, v1)[1];
         w[2] = __builtin_bit_cast(u32x2, v2)[0];
         w[3] = __builtin_bit_cast(u32x2, v2)[1];
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
-        o[db][0] = mfma16(vf, pf[0], o[db][0]);
-        o[db][1] = mfma16(vf, pf[1], o[db][1]);
+        return __builtin_bit_cast(bf16x8, w);
+      };
+      bf16x8 vf[2];
+      vf[0] = vread(0);
+#pragma unroll
+      for (int db = 0; db < 8; db++) {
+        if (db + 1 < 8) vf[(db + 1) & 1] = vread(db + 1);
+        o[db][0] = mfma16(vf[db & 1], pf[0], o[db][0]);
+        o[db][1] = mfma16(vf[db & 1], pf[1], o[db][1]);
       }
     }
   };
@@ -260,9 +279,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   auto step = [&](int t, bool masked) {
     const int ts = kt0 + t * kBN;
     const bool has_next = t + 1 < n_tiles;
-    if (has_next) load_tile(ts + kBN);
     const unsigned char *kb = smem + (t & 1) * kBufBytes;
-    tile(kb, kb + kKTile, ts, masked);
+    tile(kb, kb + kKTile, ts, masked, has_next);
     if (has_next) store_tile((t + 1) & 1);
     __syncthreads();
   };
