@@ -75,7 +75,7 @@ typedef enum swa_status {
  * have been written, slot t holds position e - ((e - t) mod window) when that
  * is >= 0; other slots hold whatever the caller put there.
  * Supported: head_dim in {16, 64, 128} for SWA_DTYPE_F32, head_dim 128 for
- * SWA_DTYPE_BF16; window >= 1; n_kv_heads >= 1.
+ * SWA_DTYPE_BF16; 1 <= window <= 2^30; n_kv_heads >= 1.
  */
 typedef struct swa_cache {
   void *k;             /* device, [n_cache][n_kv_heads][window][head_dim] */

@@ -33,6 +33,7 @@ static swa_status check_cache(const swa_cache *c, bool need_ptrs) {
   if (!c) return SWA_ERR_INVALID_ARGUMENT;
   if (c->reserved != 0) return SWA_ERR_INVALID_ARGUMENT;
   if (c->n_cache < 1 || c->n_kv_heads < 1 || c->head_dim < 1 || c->window < 1) return SWA_ERR_INVALID_ARGUMENT;
+  if (c->window > (1 << 30)) return SWA_ERR_UNSUPPORTED;  // keeps window + tile offsets inside int32
   const int eb = elt_bytes(c->dtype);
   if (eb == 0) return SWA_ERR_INVALID_ARGUMENT;
   if (need_ptrs && (!c->k || !c->v)) return SWA_ERR_INVALID_ARGUMENT;

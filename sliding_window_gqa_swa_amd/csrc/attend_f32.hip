@@ -66,7 +66,9 @@ __global__ __launch_bounds__(64 * kWaves) void attend_f32_kernel(PrefillParams p
 #pragma unroll
   for (int d = 0; d < D; d++) acc[d] = 0.f;
 
-  for (int j = lo + lane; j <= i; j += 64) {
+  const int n_keys = i - lo + 1;
+  for (int r = lane; r < n_keys; r += 64) {  // relative index: no overflow near 2^31
+    const int j = lo + r;
     const float *kr, *vr;
     if (j < ring_end) {
       const size_t off = (ring0 + (size_t)(j % W)) * D;

@@ -77,14 +77,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int W = p.cache.window;
   const int q0 = s + qt * kBQ;
   const int q_end = s + n_new;                    // one past the last query position
-  const int hi = min(q0 + kBQ, q_end) - 1;        // last key any row needs
+  // (positions go up to 2^31 - 1: sums that may pass it are formed in 64 bits)
+  const int hi = q0 + min(kBQ, q_end - q0) - 1;   // last key any row needs
   const int lo = max(0, q0 - W + 1);              // first key any row needs
   const int kt0 = (lo / kBN) * kBN;
   const int n_tiles = (hi - kt0) / kBN + 1;
-  const int nomask_lo = q0 + kBQ - W;             // tiles in [nomask_lo, q0] need no mask
+  // tiles starting at or after nomask_lo (and ending by q0) need no mask
+  const int64_t nomask_lo = (int64_t)q0 + kBQ - W;
 
   const int h = g * G + wave / kWph;
-  const int qbase = q0 + (wave % kWph) * 32;      // first query position of this wave
+  const int qoff = (wave % kWph) * 32;            // this wave's first query, relative to q0
+  const int n_rows = q_end - q0;                  // valid query positions from q0 on
   const int hq = p.n_q_heads;
   const float c = p.scale_log2;
 
@@ -93,9 +96,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   bf16x8 qf[4][2];
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
-    const int qpos = qbase + 16 * qb + (lane & 15);
-    const bool ok = qpos < q_end;
-    const uint16_t *qrow = Q + ((size_t)(tok0 + qpos - s) * hq + h) * kD + 8 * (lane >> 4);
+    const int qrel = qoff + 16 * qb + (lane & 15);
+    const bool ok = qrel < n_rows;
+    const uint16_t *qrow = Q + ((size_t)(tok0 + (q0 - s) + qrel) * hq + h) * kD + 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
       u32x4 v = {0, 0, 0, 0};
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       // key - query for this lane's first element; valid iff -W < key - query <= 0
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) {
-        const int d0 = ts + 4 * (lane >> 4) - (qbase + 16 * qb + (lane & 15)) + W - 1;
+        const int d0 = (ts - q0) + 4 * (lane >> 4) - (qoff + 16 * qb + (lane & 15)) + W - 1;
 #pragma unroll
         for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   // Tiles needing a mask form a prefix (window's lower edge) and a suffix (the
   // diagonal) of the tile range; the interior runs the unmasked body.
   //   unmasked  <=>  ts >= nomask_lo  and  ts + kBN - 1 <= q0
-  const int n_lead = min(n_tiles, max(0, (nomask_lo - kt0 + kBN - 1) / kBN));
+  const int n_lead = (int)min((int64_t)n_tiles, max((int64_t)0, (nomask_lo - kt0 + kBN - 1) / kBN));
   const int n_diag_free = (q0 - kBN + 1 - kt0) >= 0 ? (q0 - kBN + 1 - kt0) / kBN + 1 : 0;
   const int t_mid_end = max(n_lead, min(n_tiles, n_diag_free));
 
@@ -301,9 +304,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     lt += xor16(lt);
     lt += xor32(lt);
     const float inv = 1.0f / lt;
-    const int qpos = qbase + 16 * qb + (lane & 15);
-    if (qpos < q_end) {
-      uint16_t *orow = O + ((size_t)(tok0 + qpos - s) * hq + h) * kD + 4 * (lane >> 4);
+    const int qrel = qoff + 16 * qb + (lane & 15);
+    if (qrel < n_rows) {
+      uint16_t *orow = O + ((size_t)(tok0 + (q0 - s) + qrel) * hq + h) * kD + 4 * (lane >> 4);
 #pragma unroll
       for (int db = 0; db < 8; db++) {
         u32x2 w;

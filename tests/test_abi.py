@@ -93,7 +93,7 @@ def test_null_structs_are_rejected():
 @pytest.mark.parametrize("field,value,code", [
     ("window", 0, INVALID), ("n_cache", 0, INVALID), ("n_kv_heads", 0, INVALID), ("head_dim", 0, INVALID),
     ("dtype", 7, INVALID), ("reserved", 1, INVALID), ("k", FAKE + 8, INVALID), ("v", None, INVALID),
-    ("head_dim", 64, UNSUPPORTED), ("head_dim", 96, UNSUPPORTED),
+    ("head_dim", 64, UNSUPPORTED), ("head_dim", 96, UNSUPPORTED), ("window", 2**30 + 1, UNSUPPORTED),
 ])
 def test_bad_cache_descriptor(field, value, code):
     c = cache(**{field: value})

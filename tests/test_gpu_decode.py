@@ -80,3 +80,9 @@ def test_deterministic_bitwise():
     a = host_raw(run_decode(wl, cache), "bf16")
     b = host_raw(run_decode(wl, cache, write_first=False), "bf16")
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_position_next_to_int32_max(dtype):
+    d = 128 if dtype == "bf16" else 16
+    decode_case(61, [2**31 - 2, 2**31 - 5000], 4096 if dtype == "bf16" else 64, 8, 2, d, dtype)

@@ -201,3 +201,15 @@ def test_no_cache_pointers_when_every_sequence_starts_at_zero():
     out = empty((wl.total_tokens, 32, 128), "bf16")
     swa.swa_prefill_chunk(c, new_batch(wl), q, 32, kn, vn, wl.scale, out)
     check_close(host_f32(out, "bf16"), oracle_all(wl), "bf16", "no cache")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_positions_next_to_int32_max(dtype):
+    # the last position of the chunk is 2^31 - 2: every position sum stays in range
+    d = 128 if dtype == "bf16" else 64
+    top = 2**31 - 1
+    prefill_case(91, [(top - 301, 300), (top - 70, 69)], 100, 8, 2, d, dtype)
+
+
+def test_empty_sequence_inside_a_batch():
+    prefill_case(92, [(0, 130), (40, 0), (500, 77), (3, 0)], 64, 32, 8, 128, "bf16")
