@@ -11,23 +11,29 @@
 //   its keys and values.
 //
 // Design (MI355X / CDNA4):
-//   * One workgroup = (sequence, KV head g, tile of BQ query positions) x the G
-//     query heads of g: 8 waves, 32 query rows each, 256 rows per workgroup.
-//     Every K/V tile is staged ONCE in LDS and consumed by all G heads.
+//   * One workgroup = (sequence, KV head g, BQ = 256/G query positions) x the G
+//     query heads of g = 256 query rows in 8 waves of 32 rows.  Every K/V tile
+//     (64 keys) is staged ONCE in LDS and consumed by all G heads.
 //   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16.  The S^T
 //     accumulator layout (lane = query, registers = keys) is reused directly
 //     as the B operand of the PV product, so P never leaves registers; V^T is
 //     read with ds_read_b64_tr_b16 (4-key transposed loads).
-//   * K/V tiles are BN = 64 keys aligned to multiples of 64 in absolute
-//     position.  Only the tiles intersecting the workgroup's band
-//     [q0-W+1, q_last] are visited; tiles wholly inside every row's band run
-//     without a mask.  Keys outside the band are zero-filled in LDS, never
-//     loaded, so unwritten cache slots cannot reach the arithmetic.
-//   * LDS rows are padded: K rows to 272 B (consecutive rows 4 banks apart: the
-//     16-byte K reads of 8 rows cover all 32 banks), V rows to 288 B (rows 8
-//     banks apart: the 4 rows x 32 B of a transposed read of 16 lanes hit
-//     disjoint banks).  Every operand address is a per-lane base plus an
-//     immediate.  K and V are double-buffered (70 KiB), one barrier per tile.
+//   * Ping-pong: waves w and w+4 share a SIMD and belong to different groups
+//     (A = waves 0-3, B = waves 4-7).  Each tile is a softmax half-step (VALU)
+//     and a matrix half-step (PV of this tile + QK of the next, MFMA + LDS
+//     reads); group B runs one half-step behind A, so on every SIMD one wave
+//     issues MFMAs while the other runs the softmax.
+//   * Tiles go straight from global memory into LDS (global_load_lds, 16 bytes
+//     per lane): group A streams the K tiles (3 LDS slots), group B the V
+//     tiles (2 slots); no staging registers.  LDS rows are 256 B with XOR
+//     swizzles of the 16-byte chunks: K chunk ^ (row % 16) (the 16-byte K
+//     reads of 16 rows hit 16 different chunks), V chunk ^ 2 (row % 4) (the
+//     4 rows x 32 B of a 16-lane transposed read hit 8 different chunks).
+//   * Only tiles intersecting the workgroup's band [q0-W+1, q_last] are
+//     visited; only tiles crossing a row's window edge or the diagonal run the
+//     mask code.  Keys outside the band are never read from outside it: their
+//     rows are loaded from the nearest key of the band (always written data)
+//     and masked, so unwritten cache slots cannot reach the arithmetic.
 //   * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
 //   * Workgroups are ordered heaviest-first and mapped XCD-contiguously.
 #include "device_common.h"
@@ -40,19 +46,21 @@ constexpr int kD = 128;
 constexpr int kBN = 64;                       // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKRow = kD * 2 + 16;            // K rows: 256 B of data + 16 B of padding
-constexpr int kVRow = kD * 2 + 32;            // V rows: 256 B of data + 32 B of padding
-constexpr int kKTile = kBN * kKRow;
-constexpr int kVTile = kBN * kVRow;
-constexpr int kBufBytes = kKTile + kVTile;    // one K tile + one V tile
-constexpr int kLdsBytes = 2 * kBufBytes;      // double-buffered
+constexpr int kRowB = kD * 2;                 // 256-byte LDS rows
+constexpr int kTileB = kBN * kRowB;           // 16 KiB
+constexpr int kLdsBytes = 5 * kTileB;         // 3 K slots + 2 V slots
 constexpr float kRescaleSlack = 8.0f;         // log2 units: weights stay <= 256
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+// Wait for this wave's outstanding global loads (including those that write
+// LDS directly); expcnt and lgkmcnt are left unconstrained.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p) {
@@ -107,53 +115,64 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     }
   }
 
-  // ---- K/V tile staging: thread -> rows r0, r0 + 32 of a tile, 16-byte chunk cc.
-  // Keys below the chunk start come from ring slot j mod W (advanced
-  // incrementally by 64 per tile), keys from the chunk on from k_new / v_new.
-  const int r0 = tid >> 4, cc = tid & 15;
-  const uint16_t *ck = (const uint16_t *)p.cache.k, *cv = (const uint16_t *)p.cache.v;
-  const uint16_t *kn = (const uint16_t *)p.k_new, *vn = (const uint16_t *)p.v_new;
-  const int64_t ring_base = ((int64_t)crow * hkv + g) * (int64_t)W * kD + cc * 8;
-  const int64_t new_stride = (int64_t)hkv * kD;
-  const int64_t new_base = ((int64_t)(tok0 - s) * hkv + g) * kD + cc * 8;  // + j * new_stride
-  const int slot_step = kBN % W;
-  int slot[2] = {(kt0 + r0) % W, (kt0 + r0 + 32) % W};
-  u32x4 stg[4];
-  auto load_tile = [&](int ts) {
+  // ---- Tile streaming.  Group A (waves 0-3) loads K tiles, group B (waves
+  // 4-7) V tiles.  A tile is 16 loads of 1 KiB (4 rows each); wave wg of its
+  // group issues loads wg, wg+4, wg+8, wg+12, i.e. rows 4*wg + 16*m + (lane/16),
+  // and its lane writes LDS chunk (lane % 16) of that row, which holds the
+  // logical chunk (lane % 16) ^ swizzle(row) -- a per-lane constant.
+  const int grp = wave >> 2, wg = wave & 3;
+  const int row_l = 4 * wg + (lane >> 4);            // row of load m is row_l + 16 m
+  const int pchunk = lane & 15;
+  const int lchunk = grp == 0 ? (pchunk ^ (row_l & 15)) : (pchunk ^ (2 * (row_l & 3)));
+  const char *src_ring = (const char *)(grp == 0 ? p.cache.k : p.cache.v);
+  const char *src_new = (const char *)(grp == 0 ? p.k_new : p.v_new);
+  const int64_t ring_row0 = ((int64_t)crow * hkv + g) * (int64_t)W;     // ring rows of (crow, g)
+  const int64_t new_stride = (int64_t)hkv * kRowB;                     // bytes between tokens
+  const int64_t new_tok0 = (int64_t)(tok0 - s);                        // token index of position 0
+  auto load_tile = [&](unsigned char *dst, int ts) {
+    const bool all_valid = ts >= lo && ts + kBN - 1 <= hi;
+    const int ts_mod = ts % W;
+    if (all_valid && ts >= s) {
+      const char *base = src_new + ((new_tok0 + ts + row_l) * hkv + g) * (int64_t)kRowB + lchunk * 16;
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int j = ts + r0 + 32 * u;
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (j >= lo && j <= hi) {
-        const bool ring = j < s;
-        const int64_t off = ring ? ring_base + (int64_t)slot[u] * kD : new_base + (int64_t)j * new_stride;
-        const uint16_t *kp = ring ? ck : kn;
-        const uint16_t *vp = ring ? cv : vn;
-        kv = *(const u32x4 *)(kp + off);
-        vv = *(const u32x4 *)(vp + off);
+      for (int m = 0; m < 4; m++)
+        __builtin_amdgcn_global_load_lds(base + (int64_t)(16 * m) * new_stride,
+                                         (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
+    } else if (all_valid && ts + kBN - 1 < s && ts_mod + kBN <= W) {
+      const char *base = src_ring + (ring_row0 + ts_mod + row_l) * kRowB + lchunk * 16;
+#pragma unroll
+      for (int m = 0; m < 4; m++)
+        __builtin_amdgcn_global_load_lds(base + 16 * m * kRowB, (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
+    } else {
+      // edge tile: rows outside [lo, hi] read the nearest key of the band
+#pragma unroll
+      for (int m = 0; m < 4; m++) {
+        const int j = min(max(ts + row_l + 16 * m, lo), hi);
+        const char *src = j < s ? src_ring + (ring_row0 + j % W) * kRowB
+                                : src_new + ((new_tok0 + j) * hkv + g) * (int64_t)kRowB;
+        __builtin_amdgcn_global_load_lds(src + lchunk * 16, (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
       }
-      stg[u] = kv;
-      stg[2 + u] = vv;
-      slot[u] += slot_step;
-      if (slot[u] >= W) slot[u] -= W;
     }
   };
-  const int kst = r0 * kKRow + cc * 16, vst = r0 * kVRow + cc * 16;
-  auto store_tile = [&](int buf) {
-    unsigned char *kb = smem + buf * kBufBytes;
-    unsigned char *vb = kb + kKTile;
-    *(u32x4 *)(kb + kst) = stg[0];
-    *(u32x4 *)(kb + kst + 32 * kKRow) = stg[1];
-    *(u32x4 *)(vb + vst) = stg[2];
-    *(u32x4 *)(vb + vst + 32 * kVRow) = stg[3];
-  };
-  // LDS byte offsets of this lane's MFMA operand reads.  With padded rows every
-  // read is this per-lane base plus a compile-time constant.
-  //   K (A operand of S^T): row 16*kbi + lane%16, columns 32*ks + 8*(lane/16) .. +8
-  //   V (transposed reads): rows 32*kk + 4*(lane/16) + (lane%16)/4 (+16),
-  //                         columns 16*db + 4*(lane%4) .. +4
-  const int k_lane = (lane & 15) * kKRow + (lane >> 4) * 16;
-  const int v_lane = (4 * (lane >> 4) + ((lane & 15) >> 2)) * kVRow + 8 * (lane & 3);
+  auto kslot = [&](int i) { return smem + i * kTileB; };
+  auto vslot = [&](int i) { return smem + (3 + i) * kTileB; };
+
+  // LDS offsets of this lane's MFMA operand reads.
+  //   K (A operand of S^T): row 16*kbi + lane%16, logical chunk 4*ks + lane/16
+  //     -> k_off[ks] + 4096*kbi
+  //   V (transposed reads): rows 32*kk + 16*half + 4*(lane/16) + (lane%16)/4,
+  //     columns 16*db + 4*(lane%4) .. +4 -> v_off[db%4] + 128*(db/4) + rows*256
+  int k_off[4], v_off[4];
+  {
+    const int r = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) k_off[ks] = r * kRowB + (((4 * ks + (lane >> 4)) ^ r) << 4);
+    const int vr = 4 * (lane >> 4) + ((lane & 15) >> 2);
+    const int j = vr & 3;
+    const int vb = vr * kRowB + 16 * ((lane & 3) >> 1) + 8 * (lane & 1);
+#pragma unroll
+    for (int dl = 0; dl < 4; dl++) v_off[dl] = vb + 32 * (dl ^ j);
+  }
 
   f32x4 o[8][2];
 #pragma unroll
@@ -162,25 +181,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     for (int qb = 0; qb < 2; qb++) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY};  // running max, log2 units
   float l[2] = {0.f, 0.f};              // this lane's share of the row sums
+  f32x4 sa[4][2];                       // S^T of the tile in flight: 4 key blocks x 2 query blocks
+  u32x4 pw[2][2];                       // P^T (bf16 pairs) of the softmaxed tile: [32-key slice][qb]
 
-  // One K/V tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
-  auto tile = [&](const unsigned char *kb, const unsigned char *vb, int ts, bool masked, bool has_next) {
-    f32x4 sa[4][2];
+  // S^T = K Q^T; K fragments are read one 32-wide d-step ahead of their MFMAs
+  auto qk = [&](const unsigned char *kb) {
 #pragma unroll
     for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // K fragments are read one 32-wide d-step ahead of the MFMAs that use them,
-    // so the LDS latency overlaps the matrix work of the previous step.
     bf16x8 kf[2][4];
 #pragma unroll
-    for (int kbi = 0; kbi < 4; kbi++) kf[0][kbi] = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kKRow);
+    for (int kbi = 0; kbi < 4; kbi++) kf[0][kbi] = *(const bf16x8 *)(kb + k_off[0] + 4096 * kbi);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
       if (ks + 1 < 4) {
 #pragma unroll
-        for (int kbi = 0; kbi < 4; kbi++)
-          kf[(ks + 1) & 1][kbi] = *(const bf16x8 *)(kb + k_lane + 16 * kbi * kKRow + 64 * (ks + 1));
+        for (int kbi = 0; kbi < 4; kbi++) kf[(ks + 1) & 1][kbi] = *(const bf16x8 *)(kb + k_off[ks + 1] + 4096 * kbi);
       }
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++) {
@@ -188,11 +205,45 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         sa[kbi][1] = mfma16(kf[ks & 1][kbi], qf[ks][1], sa[kbi][1]);
       }
     }
-    // the next tile's global loads are issued here, after the K fragments of
-    // this tile are consumed (shorter register live ranges); their latency is
-    // covered by the softmax and PV work below
-    if (has_next) load_tile(ts + kBN);
+  };
+
+  // O^T += V^T P^T; V fragments are read one 16-column block ahead
+  auto pv = [&](const unsigned char *vbase) {
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      auto vread = [&](int db) {
+        const unsigned char *va = vbase + v_off[db & 3] + 128 * (db >> 2) + 32 * kk * kRowB;
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowB));
+        u32x4 w;
+        w[0] = __builtin_bit_cast(u32x2, v1)[0];
+        w[1] = __builtin_bit_cast(u32x2, v1)[1];
+        w[2] = __builtin_bit_cast(u32x2, v2)[0];
+        w[3] = __builtin_bit_cast(u32x2, v2)[1];
+        return __builtin_bit_cast(bf16x8, w);
+      };
+      const bf16x8 p0 = __builtin_bit_cast(bf16x8, pw[kk][0]);
+      const bf16x8 p1 = __builtin_bit_cast(bf16x8, pw[kk][1]);
+      bf16x8 vf[2];
+      vf[0] = vread(0);
+#pragma unroll
+      for (int db = 0; db < 8; db++) {
+        if (db + 1 < 8) vf[(db + 1) & 1] = vread(db + 1);
+        o[db][0] = mfma16(vf[db & 1], p0, o[db][0]);
+        o[db][1] = mfma16(vf[db & 1], p1, o[db][1]);
+      }
+    }
+  };
+
+  // mask (edge tiles), online softmax, P^T as bf16 into pw, row sums.
+  // A query's 64 keys sit in lanes l, l^16, l^32, l^48.  The running max m is
+  // kept in log2 units (score * scale * log2 e) and only moves when a tile's
+  // max exceeds it by more than kRescaleSlack: the weights then stay
+  // <= 2^kRescaleSlack, O/l are rescaled only on those (rare) tiles, and the
+  // result is unchanged because O and l share m.
+  auto softmax = [&](int ts, bool masked) {
     if (masked) {
+      __asm__ volatile("");  // keep this a branch: only edge tiles pay for the mask
       // key - query for this lane's first element; valid iff -W < key - query <= 0
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) {
@@ -204,11 +255,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             if ((unsigned)(d0 + 16 * kbi + i) >= (unsigned)W) sa[kbi][qb][i] = -INFINITY;
       }
     }
-    // Online softmax per query; a query's 64 keys sit in lanes l, l^16, l^32, l^48.
-    // The running max m is kept in log2 units (score * scale * log2 e) and only
-    // moves when a tile's max exceeds it by more than kRescaleSlack: the
-    // weights then stay <= 2^kRescaleSlack, the O/l rescale runs only on those
-    // (rare) tiles, and the result is unchanged because O and l share m.
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
       float mt = -INFINITY;
@@ -232,69 +278,64 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
         for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kbi][qb][i], c, -mc));
-    }
-    // O^T += V^T P^T over two 32-key slices
 #pragma unroll
-    for (int kk = 0; kk < 2; kk++) {
-      bf16x8 pf[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; qb++) {
+      for (int kk = 0; kk < 2; kk++) {
         u32x4 w;
         w[0] = pack_bf16(sa[2 * kk][qb][0], sa[2 * kk][qb][1]);
         w[1] = pack_bf16(sa[2 * kk][qb][2], sa[2 * kk][qb][3]);
         w[2] = pack_bf16(sa[2 * kk + 1][qb][0], sa[2 * kk + 1][qb][1]);
         w[3] = pack_bf16(sa[2 * kk + 1][qb][2], sa[2 * kk + 1][qb][3]);
-        pf[qb] = __builtin_bit_cast(bf16x8, w);
+        pw[kk][qb] = w;
         // row sum of the bf16-rounded weights, i.e. of exactly what enters P V
 #pragma unroll
         for (int e = 0; e < 4; e++) l[qb] = fdot2_bf16(w[e], kBf16OnePair, l[qb]);
       }
-      // V fragments are read one 16-column block ahead of their MFMAs.
-      auto vread = [&](int db) {
-        const unsigned char *va = vb + v_lane + 32 * kk * kVRow + 32 * db;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kVRow));
-        u32x4 w;
-        w[0] = __builtin_bit_cast(u32x2, v1)[0];
-        w[1] = __builtin_bit_cast(u32x2, v1)[1];
-        w[2] = __builtin_bit_cast(u32x2, v2)[0];
-        w[3] = __builtin_bit_cast(u32x2, v2)[1];
-        return __builtin_bit_cast(bf16x8, w);
-      };
-      bf16x8 vf[2];
-      vf[0] = vread(0);
-#pragma unroll
-      for (int db = 0; db < 8; db++) {
-        if (db + 1 < 8) vf[(db + 1) & 1] = vread(db + 1);
-        o[db][0] = mfma16(vf[db & 1], pf[0], o[db][0]);
-        o[db][1] = mfma16(vf[db & 1], pf[1], o[db][1]);
-      }
     }
   };
 
-  // Tiles needing a mask form a prefix (window's lower edge) and a suffix (the
-  // diagonal) of the tile range; the interior runs the unmasked body.
+  // ---- Schedule.  Tile t = softmax half-step V_t and matrix half-step
+  // M_t = { O += P(t) V(t);  S = K(t+1) Q^T }, separated by barriers; group B
+  // runs one half-step behind group A.  During V_t group A streams K(t+2)
+  // into K slot (t+2) mod 3 and group B streams V(t+1) into V slot (t+1) mod 2.
+  // With A's V_t in half-step 2t and B's in 2t+1 (M_t one later), a slot is
+  // rewritten only after its last reader (B's M of two tiles back, or of the
+  // previous tile for V) has passed a barrier, and each tile is complete (its
+  // loads waited for) one barrier before its first reader.  Every wave executes
+  // the same number of barriers.
+  //
+  // Tiles needing a mask form a prefix (the window's lower edge) and a suffix
+  // (the diagonal) of the tile range; the interior runs without mask code.
   //   unmasked  <=>  ts >= nomask_lo  and  ts + kBN - 1 <= q0
   const int n_lead = (int)min((int64_t)n_tiles, max((int64_t)0, (nomask_lo - kt0 + kBN - 1) / kBN));
   const int n_diag_free = (q0 - kBN + 1 - kt0) >= 0 ? (q0 - kBN + 1 - kt0) / kBN + 1 : 0;
   const int t_mid_end = max(n_lead, min(n_tiles, n_diag_free));
 
   auto step = [&](int t, bool masked) {
-    const int ts = kt0 + t * kBN;
-    const bool has_next = t + 1 < n_tiles;
-    const unsigned char *kb = smem + (t & 1) * kBufBytes;
-    tile(kb, kb + kKTile, ts, masked, has_next);
-    if (has_next) store_tile((t + 1) & 1);
+    const int nt = grp == 0 ? t + 2 : t + 1;  // the tile this group streams now
+    if (nt < n_tiles) load_tile(grp == 0 ? kslot(nt % 3) : vslot(nt & 1), kt0 + nt * kBN);
+    softmax(kt0 + t * kBN, masked);
+    wait_vmem();
+    __syncthreads();
+    pv(vslot(t & 1));
+    if (t + 1 < n_tiles) qk(kslot((t + 1) % 3));
     __syncthreads();
   };
 
-  load_tile(kt0);
-  store_tile(0);
+  if (grp == 0) {
+    load_tile(kslot(0), kt0);
+    if (n_tiles > 1) load_tile(kslot(1), kt0 + kBN);
+  } else {
+    load_tile(vslot(0), kt0);
+  }
+  wait_vmem();
   __syncthreads();
+  if (grp == 1) __builtin_amdgcn_s_barrier();  // group B: half a step behind
+  qk(kslot(0));
   int t = 0;
   for (; t < n_lead; t++) step(t, true);
   for (; t < t_mid_end; t++) step(t, false);
   for (; t < n_tiles; t++) step(t, true);
+  if (grp == 0) __builtin_amdgcn_s_barrier();  // group A: matches B's extra barrier
 
   // epilogue: finish the row sums across the 4 lane groups, normalise, store bf16
   uint16_t *O = (uint16_t *)p.out;
