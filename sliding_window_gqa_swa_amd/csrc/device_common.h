@@ -51,34 +51,38 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-// Value of lane (l ^ 16) / (l ^ 32), through the gfx950 row-swap instructions
-// (plain VALU, no LDS round trip).  permlane16_swap(x, x) returns x with rows
-// 1 and 3 replaced by rows 0 and 2, and x with rows 0 and 2 replaced by rows
-// 1 and 3 (a row is 16 lanes); lane l of the result that is not its own row
-// holds the value of lane l ^ 16.  Likewise for halves of 32 lanes.
-__device__ __forceinline__ float xor16(float x) {
+// max / sum over the lane pair {l, l ^ 16} (or {l, l ^ 32}), through the gfx950
+// row-swap instructions (plain VALU, no LDS round trip).  permlane16_swap(x, x)
+// returns x with rows 1 and 3 replaced by rows 0 and 2, and x with rows 0 and 2
+// replaced by rows 1 and 3 (a row is 16 lanes; likewise halves of 32 lanes for
+// permlane32_swap).  In every lane the two results are its own value and its
+// partner's, so no lane select is needed and both lanes of a pair get the same
+// value.
+__device__ __forceinline__ float max_pair16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const int lane = __lane_id();
-  return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float xor32(float x) {
+__device__ __forceinline__ float max_pair32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const int lane = __lane_id();
-  return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Reductions over lanes {l, l^8, l^16, ...}: combine groups of 8 lanes.
 __device__ __forceinline__ float max_over_groups8(float x) {
   x = fmaxf(x, dpp_f<kDppRowRor8>(x));
-  x = fmaxf(x, xor16(x));
-  x = fmaxf(x, xor32(x));
-  return x;
+  return max_pair32(max_pair16(x));
 }
 __device__ __forceinline__ float sum_over_groups8(float x) {
   x += dpp_f<kDppRowRor8>(x);
-  x += xor16(x);
-  x += xor32(x);
-  return x;
+  return add_pair32(add_pair16(x));
 }
 
 // Workgroups are dispatched to the XCDs round-robin (id mod 8).  Give each XCD

@@ -39,6 +39,8 @@
 #include "device_common.h"
 #include "swa_internal.h"
 
+#include <type_traits>
+
 namespace swa {
 namespace {
 
@@ -68,7 +70,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   constexpr int kBQ = 32 * kWph;    // query positions per workgroup
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave choices scalar
   const int work = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, p.n_work));
   const int tps = p.tiles_per_seq;
   const int qt = tps - 1 - (work % tps);  // heaviest (latest) query tile first
@@ -129,20 +132,24 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int64_t ring_row0 = ((int64_t)crow * hkv + g) * (int64_t)W;     // ring rows of (crow, g)
   const int64_t new_stride = (int64_t)hkv * kRowB;                     // bytes between tokens
   const int64_t new_tok0 = (int64_t)(tok0 - s);                        // token index of position 0
-  auto load_tile = [&](unsigned char *dst, int ts) {
+  const uint32_t lane_off_new = (uint32_t)(row_l * hkv * kRowB + lchunk * 16);
+  const uint32_t lane_off_ring = (uint32_t)(row_l * kRowB + lchunk * 16);
+  auto load_tile = [&](unsigned char *dst, int ts) __attribute__((always_inline)) {
     const bool all_valid = ts >= lo && ts + kBN - 1 <= hi;
     const int ts_mod = ts % W;
+    // fast paths: a uniform base (scalar registers) plus this lane's 32-bit offset
     if (all_valid && ts >= s) {
-      const char *base = src_new + ((new_tok0 + ts + row_l) * hkv + g) * (int64_t)kRowB + lchunk * 16;
+      const char *base = src_new + ((new_tok0 + ts) * hkv + g) * (int64_t)kRowB;
 #pragma unroll
       for (int m = 0; m < 4; m++)
-        __builtin_amdgcn_global_load_lds(base + (int64_t)(16 * m) * new_stride,
+        __builtin_amdgcn_global_load_lds(base + (int64_t)(16 * m) * new_stride + lane_off_new,
                                          (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
     } else if (all_valid && ts + kBN - 1 < s && ts_mod + kBN <= W) {
-      const char *base = src_ring + (ring_row0 + ts_mod + row_l) * kRowB + lchunk * 16;
+      const char *base = src_ring + (ring_row0 + ts_mod) * kRowB;
 #pragma unroll
       for (int m = 0; m < 4; m++)
-        __builtin_amdgcn_global_load_lds(base + 16 * m * kRowB, (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(base + 16 * m * kRowB + lane_off_ring,
+                                         (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
     } else {
       // edge tile: rows outside [lo, hi] read the nearest key of the band
 #pragma unroll
@@ -154,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       }
     }
   };
-  auto kslot = [&](int i) { return smem + i * kTileB; };
-  auto vslot = [&](int i) { return smem + (3 + i) * kTileB; };
+  auto kslot = [&](int i) __attribute__((always_inline)) { return smem + i * kTileB; };
+  auto vslot = [&](int i) __attribute__((always_inline)) { return smem + (3 + i) * kTileB; };
 
   // LDS offsets of this lane's MFMA operand reads.
   //   K (A operand of S^T): row 16*kbi + lane%16, logical chunk 4*ks + lane/16
@@ -184,53 +191,48 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   f32x4 sa[4][2];                       // S^T of the tile in flight: 4 key blocks x 2 query blocks
   u32x4 pw[2][2];                       // P^T (bf16 pairs) of the softmaxed tile: [32-key slice][qb]
 
-  // S^T = K Q^T; K fragments are read one 32-wide d-step ahead of their MFMAs
-  auto qk = [&](const unsigned char *kb) {
+  // S^T = K Q^T (the order of LDS reads and MFMAs is set by the half-step schedule)
+  auto qk = [&](const unsigned char *kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int kbi = 0; kbi < 4; kbi++) kf[0][kbi] = *(const bf16x8 *)(kb + k_off[0] + 4096 * kbi);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-      if (ks + 1 < 4) {
-#pragma unroll
-        for (int kbi = 0; kbi < 4; kbi++) kf[(ks + 1) & 1][kbi] = *(const bf16x8 *)(kb + k_off[ks + 1] + 4096 * kbi);
-      }
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++) {
-        sa[kbi][0] = mfma16(kf[ks & 1][kbi], qf[ks][0], sa[kbi][0]);
-        sa[kbi][1] = mfma16(kf[ks & 1][kbi], qf[ks][1], sa[kbi][1]);
+        const bf16x8 kf = *(const bf16x8 *)(kb + k_off[ks] + 4096 * kbi);
+        sa[kbi][0] = mfma16(kf, qf[ks][0], sa[kbi][0]);
+        sa[kbi][1] = mfma16(kf, qf[ks][1], sa[kbi][1]);
       }
     }
   };
 
-  // O^T += V^T P^T; V fragments are read one 16-column block ahead
-  auto pv = [&](const unsigned char *vbase) {
+  // V^T fragment for O^T += V^T P^T: 16 d-columns (block db) x 32 keys (slice kk)
+  // of the V tile at vbase, as two 4-key transposed reads per lane.
+  auto vread = [&](const unsigned char *vbase, int kk, int db) __attribute__((always_inline)) {
+    const unsigned char *va = vbase + v_off[db & 3] + 128 * (db >> 2) + 32 * kk * kRowB;
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
+    const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowB));
+    u32x4 w;
+    w[0] = __builtin_bit_cast(u32x2, v1)[0];
+    w[1] = __builtin_bit_cast(u32x2, v1)[1];
+    w[2] = __builtin_bit_cast(u32x2, v2)[0];
+    w[3] = __builtin_bit_cast(u32x2, v2)[1];
+    return __builtin_bit_cast(bf16x8, w);
+  };
+
+  // O^T += V^T P^T (order of reads and MFMAs as for qk)
+  auto pv = [&](const unsigned char *vbase) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) {
-      auto vread = [&](int db) {
-        const unsigned char *va = vbase + v_off[db & 3] + 128 * (db >> 2) + 32 * kk * kRowB;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowB));
-        u32x4 w;
-        w[0] = __builtin_bit_cast(u32x2, v1)[0];
-        w[1] = __builtin_bit_cast(u32x2, v1)[1];
-        w[2] = __builtin_bit_cast(u32x2, v2)[0];
-        w[3] = __builtin_bit_cast(u32x2, v2)[1];
-        return __builtin_bit_cast(bf16x8, w);
-      };
       const bf16x8 p0 = __builtin_bit_cast(bf16x8, pw[kk][0]);
       const bf16x8 p1 = __builtin_bit_cast(bf16x8, pw[kk][1]);
-      bf16x8 vf[2];
-      vf[0] = vread(0);
 #pragma unroll
       for (int db = 0; db < 8; db++) {
-        if (db + 1 < 8) vf[(db + 1) & 1] = vread(db + 1);
-        o[db][0] = mfma16(vf[db & 1], p0, o[db][0]);
-        o[db][1] = mfma16(vf[db & 1], p1, o[db][1]);
+        const bf16x8 vf = vread(vbase, kk, db);
+        o[db][0] = mfma16(vf, p0, o[db][0]);
+        o[db][1] = mfma16(vf, p1, o[db][1]);
       }
     }
   };
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   // max exceeds it by more than kRescaleSlack: the weights then stay
   // <= 2^kRescaleSlack, O/l are rescaled only on those (rare) tiles, and the
   // result is unchanged because O and l share m.
-  auto softmax = [&](int ts, bool masked) {
+  auto softmax = [&](int ts, bool masked) __attribute__((always_inline)) {
     if (masked) {
       __asm__ volatile("");  // keep this a branch: only edge tiles pay for the mask
       // key - query for this lane's first element; valid iff -W < key - query <= 0
@@ -261,8 +263,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++)
         mt = fmaxf(mt, fmaxf(fmaxf(sa[kbi][qb][0], sa[kbi][qb][1]), fmaxf(sa[kbi][qb][2], sa[kbi][qb][3])));
-      mt = fmaxf(mt, xor16(mt));
-      mt = fmaxf(mt, xor32(mt));
+      mt = max_pair32(max_pair16(mt));
       const float mts = mt * c;
       const bool upd = mts > m[qb] + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(upd)) {
@@ -310,14 +311,34 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int n_diag_free = (q0 - kBN + 1 - kt0) >= 0 ? (q0 - kBN + 1 - kt0) / kBN + 1 : 0;
   const int t_mid_end = max(n_lead, min(n_tiles, n_diag_free));
 
-  auto step = [&](int t, bool masked) {
+  // Order of the matrix half-step's 48 LDS reads (32 V, then 16 K) and 64
+  // MFMAs (32 PV, then 32 QK): eight reads first, then two MFMAs and two reads
+  // alternately, so reads run about four MFMA pairs ahead of their consumers
+  // and the K reads of the next QK overlap the tail of PV.  (The compiler may
+  // still move the last QK MFMAs past the closing barrier; measured, that
+  // beats keeping them inside.)
+  auto schedule_matrix_half_step = [&]() __attribute__((always_inline)) {
+    constexpr int kReads = 48, kLead = 8, kPairs = (kReads - kLead) / 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // 0x100: LDS reads
+#pragma unroll
+    for (int i = 0; i < kPairs; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // 0x008: MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 64 - 2 * kPairs, 0);
+  };
+
+  auto step = [&](int t, bool masked, auto with_qk) __attribute__((always_inline)) {
     const int nt = grp == 0 ? t + 2 : t + 1;  // the tile this group streams now
     if (nt < n_tiles) load_tile(grp == 0 ? kslot(nt % 3) : vslot(nt & 1), kt0 + nt * kBN);
     softmax(kt0 + t * kBN, masked);
     wait_vmem();
     __syncthreads();
     pv(vslot(t & 1));
-    if (t + 1 < n_tiles) qk(kslot((t + 1) % 3));
+    if constexpr (decltype(with_qk)::value) {
+      qk(kslot((t + 1) % 3));
+      schedule_matrix_half_step();
+    }
     __syncthreads();
   };
 
@@ -331,10 +352,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   __syncthreads();
   if (grp == 1) __builtin_amdgcn_s_barrier();  // group B: half a step behind
   qk(kslot(0));
+  // every tile but the last also computes the scores of its successor
+  constexpr std::true_type kNext{};
+  constexpr std::false_type kLast{};
+  const int t_last = n_tiles - 1;
   int t = 0;
-  for (; t < n_lead; t++) step(t, true);
-  for (; t < t_mid_end; t++) step(t, false);
-  for (; t < n_tiles; t++) step(t, true);
+  for (; t < min(n_lead, t_last); t++) step(t, true, kNext);
+  for (; t < min(t_mid_end, t_last); t++) step(t, false, kNext);
+  for (; t < t_last; t++) step(t, true, kNext);
+  step(t_last, !(t_last >= n_lead && t_last < t_mid_end), kLast);
   if (grp == 0) __builtin_amdgcn_s_barrier();  // group A: matches B's extra barrier
 
   // epilogue: finish the row sums across the 4 lane groups, normalise, store bf16
@@ -342,8 +368,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
     float lt = l[qb];
-    lt += xor16(lt);
-    lt += xor32(lt);
+    lt = add_pair32(add_pair16(lt));
     const float inv = 1.0f / lt;
     const int qrel = qoff + 16 * qb + (lane & 15);
     if (qrel < n_rows) {
