@@ -27,8 +27,10 @@
 //     per lane): group A streams the K tiles (3 LDS slots), group B the V
 //     tiles (2 slots); no staging registers.  LDS rows are 256 B with XOR
 //     swizzles of the 16-byte chunks: K chunk ^ (row % 16) (the 16-byte K
-//     reads of 16 rows hit 16 different chunks), V chunk ^ 2 (row % 4) (the
-//     4 rows x 32 B of a 16-lane transposed read hit 8 different chunks).
+//     reads of 16 rows hit 16 different chunks), V chunk ^ (2 (row % 4) +
+//     8 ((row / 4) % 2)): a transposed read of 32 lanes covers rows 8k..8k+7,
+//     32 B each, and these land in 8 different 32-byte segments, i.e. all 64
+//     banks once.
 //   * Only tiles intersecting the workgroup's band [q0-W+1, q_last] are
 //     visited; only tiles crossing a row's window edge or the diagonal run the
 //     mask code.  Keys outside the band are never read from outside it: their
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int grp = wave >> 2, wg = wave & 3;
   const int row_l = 4 * wg + (lane >> 4);            // row of load m is row_l + 16 m
   const int pchunk = lane & 15;
-  const int lchunk = grp == 0 ? (pchunk ^ (row_l & 15)) : (pchunk ^ (2 * (row_l & 3)));
+  const int lchunk = grp == 0 ? (pchunk ^ (row_l & 15)) : (pchunk ^ (2 * (row_l & 3)) ^ (8 * ((row_l >> 2) & 1)));
   const char *src_ring = (const char *)(grp == 0 ? p.cache.k : p.cache.v);
   const char *src_new = (const char *)(grp == 0 ? p.k_new : p.v_new);
   const int64_t ring_row0 = ((int64_t)crow * hkv + g) * (int64_t)W;     // ring rows of (crow, g)
@@ -168,17 +170,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   //   K (A operand of S^T): row 16*kbi + lane%16, logical chunk 4*ks + lane/16
   //     -> k_off[ks] + 4096*kbi
   //   V (transposed reads): rows 32*kk + 16*half + 4*(lane/16) + (lane%16)/4,
-  //     columns 16*db + 4*(lane%4) .. +4 -> v_off[db%4] + 128*(db/4) + rows*256
-  int k_off[4], v_off[4];
+  //     columns 16*db + 4*(lane%4) .. +4 -> v_off[db/4][db%4] + rows*256
+  int k_off[4], v_off[2][4];
   {
     const int r = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) k_off[ks] = r * kRowB + (((4 * ks + (lane >> 4)) ^ r) << 4);
     const int vr = 4 * (lane >> 4) + ((lane & 15) >> 2);
-    const int j = vr & 3;
-    const int vb = vr * kRowB + 16 * ((lane & 3) >> 1) + 8 * (lane & 1);
+    const int j = vr & 3, hv = (vr >> 2) & 1;
+    const int vb = vr * kRowB + 8 * (lane & 3);
 #pragma unroll
-    for (int dl = 0; dl < 4; dl++) v_off[dl] = vb + 32 * (dl ^ j);
+    for (int dl = 0; dl < 4; dl++) {
+      v_off[0][dl] = vb + 32 * (dl ^ j) + 128 * hv;
+      v_off[1][dl] = vb + 32 * (dl ^ j) + 128 * (hv ^ 1);
+    }
   }
 
   f32x4 o[8][2];
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   // V^T fragment for O^T += V^T P^T: 16 d-columns (block db) x 32 keys (slice kk)
   // of the V tile at vbase, as two 4-key transposed reads per lane.
   auto vread = [&](const unsigned char *vbase, int kk, int db) __attribute__((always_inline)) {
-    const unsigned char *va = vbase + v_off[db & 3] + 128 * (db >> 2) + 32 * kk * kRowB;
+    const unsigned char *va = vbase + v_off[db >> 2][db & 3] + 32 * kk * kRowB;
     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
     const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowB));
     u32x4 w;
