@@ -128,6 +128,28 @@ def suite(up, pq, pk, pv, pout, scale, reps: int):
         t_w = time_ms(lambda: swa.swa_cache_write(cache, batch, kc, vc), reps)
         fl = 4.0 * 128 * 32 * B * band_pairs(s, C, W)
         chunks.append((t_p, t_w, fl))
+    # chunk-size sweep over the same sequences (the pages advise chunk = window):
+    # prefill + cache write of all chunks, and the activation buffers one call needs
+    sweep = {}
+    for cs in (W // 4, W // 2, W, 2 * W):
+        cache.k.zero_()
+        cache.v.zero_()
+        t_tot, w_tot = 0.0, 0.0
+        ob = torch.empty((B * cs, 32, 128), dtype=torch.bfloat16, device=dev)
+        for s in range(0, N, cs):
+            batch = swa.Batch([cs] * B, [s] * B, list(range(B)))
+            qc = qd[:, s:s + cs].reshape(B * cs, 32, 128).contiguous()
+            kc = kd[:, s:s + cs].reshape(B * cs, 8, 128).contiguous()
+            vc = vd[:, s:s + cs].reshape(B * cs, 8, 128).contiguous()
+            t_tot += time_ms(lambda: swa.swa_prefill_chunk(cache, batch, qc, 32, kc, vc, scale, ob), reps)
+            w_tot += time_ms(lambda: swa.swa_cache_write(cache, batch, kc, vc), reps)
+        fl = 4.0 * 128 * 32 * B * band_pairs(0, N, W)
+        act = B * cs * (32 + 8 + 8 + 32) * 128 * 2  # q, k_new, v_new, out of one call
+        sweep[f"C={cs}"] = {"prefill_ms": round(t_tot, 3), "prefill_tflops": round(fl / t_tot / 1e9, 1),
+                            "cache_write_ms": round(w_tot, 3), "calls": N // cs,
+                            "activation_mib_per_call": round(act / 2**20, 1)}
+        del ob
+    res["chunk_sweep_4x32k_w4096"] = sweep
     del qd, kd, vd
     tot_ms = sum(c[0] for c in chunks)
     tot_fl = sum(c[2] for c in chunks)

@@ -1,0 +1,120 @@
+"""Stacked sliding-window layers on the GPU: a multi-layer rolling cache and the
+receptive field of k layers.
+
+Mistral 7B (Chinese translation), section 2:
+  * paragraph "Sliding Window Attention" and the Figure 1 caption: a query
+    attends to W positions ending at itself, so each layer moves information
+    forward by at most W-1 positions and after k layers position i depends on
+    positions i - k(W-1) .. i only;
+  * paragraph "Rolling Buffer Cache": every layer keeps its own W-slot ring.
+    Here the rings of all layers live in one [L][n_cache][Hkv][W][D] tensor and
+    each layer's swa_cache points at its slice;
+  * paragraph "Pre-fill and Chunking": the prompt goes through all layers chunk
+    by chunk, each chunk attending to the layer's ring and to itself.
+
+The layers around attention are synthetic stand-ins (fixed random projections
+and a residual connection, fp32 torch matmuls); attention and the cache writes
+run in the library.  Nothing here is compared with the oracle: the pins are
+exact properties (which outputs may change, what each ring slice holds).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import sliding_window_gqa_swa_amd as swa
+from helpers import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def make_weights(n_layers, hq, hkv, d, seed):
+    t = torch()
+    g = t.Generator(device="cpu").manual_seed(seed)
+    e = hq * d
+
+    def w(a, b):
+        return (t.randn(a, b, generator=g) / math.sqrt(a)).cuda()
+
+    return [(w(e, hq * d), w(e, hkv * d), w(e, hkv * d), w(hq * d, e)) for _ in range(n_layers)]
+
+
+def run_stack(x0, weights, window, chunk, dtype, hq, hkv, d):
+    """Chunk-major pass of x0 [n][hq*d] through the layers.  Returns the final
+    activations, the multi-layer cache tensors and every layer's K/V rows."""
+    t = torch()
+    n = x0.shape[0]
+    n_layers = len(weights)
+    tdt = t.bfloat16 if dtype == "bf16" else t.float32
+    kk = t.full((n_layers, 1, hkv, window, d), float("nan"), dtype=tdt, device="cuda")
+    vv = t.full((n_layers, 1, hkv, window, d), float("nan"), dtype=tdt, device="cuda")
+    caches = [swa.Cache(kk[layer], vv[layer]) for layer in range(n_layers)]
+    k_rows = [t.empty((n, hkv, d), dtype=tdt, device="cuda") for _ in range(n_layers)]
+    v_rows = [t.empty((n, hkv, d), dtype=tdt, device="cuda") for _ in range(n_layers)]
+    out = t.empty_like(x0)
+    scale = 1.0 / math.sqrt(d)
+    for s in range(0, n, chunk):
+        c = min(chunk, n - s)
+        batch = swa.Batch([c], [s], [0])
+        x = x0[s:s + c]
+        for layer, (wq, wk, wv, wo) in enumerate(weights):
+            q = (x @ wq).to(tdt).reshape(c, hq, d).contiguous()
+            k = (x @ wk).to(tdt).reshape(c, hkv, d).contiguous()
+            v = (x @ wv).to(tdt).reshape(c, hkv, d).contiguous()
+            a = t.empty((c, hq, d), dtype=tdt, device="cuda")
+            swa.swa_prefill_chunk(caches[layer], batch, q, hq, k, v, scale, a)
+            swa.swa_cache_write(caches[layer], batch, k, v)
+            k_rows[layer][s:s + c] = k
+            v_rows[layer][s:s + c] = v
+            x = x + a.float().reshape(c, hq * d) @ wo
+        out[s:s + c] = x
+    t.cuda.synchronize()
+    return out, kk, vv, k_rows, v_rows
+
+
+CASES = [("f32", 16, 4, 6), ("bf16", 128, 8, 16)]
+
+
+@pytest.mark.parametrize("dtype,d,window,chunk", CASES)
+def test_receptive_field_of_stacked_layers(dtype, d, window, chunk):
+    t = torch()
+    n_layers, hq, hkv, n = 3, 2, 1, 64
+    weights = make_weights(n_layers, hq, hkv, d, seed=7)
+    g = t.Generator(device="cpu").manual_seed(8)
+    x0 = t.randn(n, hq * d, generator=g).cuda()
+    base = run_stack(x0, weights, window, chunk, dtype, hq, hkv, d)[0]
+    reach = n_layers * (window - 1)
+    for j in (0, 17, n - 1):
+        x1 = x0.clone()
+        x1[j] += 1.0
+        pert = run_stack(x1, weights, window, chunk, dtype, hq, hkv, d)[0]
+        changed = (pert != base).any(dim=1).cpu().numpy()
+        inside = np.array([j <= i <= j + reach for i in range(n)])
+        # outside the receptive field nothing may move, not even by one ulp
+        assert not changed[~inside].any(), (j, np.nonzero(changed & ~inside))
+        if dtype == "f32":
+            # fp32 resolves the whole field, up to its far edge j + k(W-1)
+            assert changed[inside].all(), (j, np.nonzero(inside & ~changed))
+        else:
+            # bf16: at least the first layer's direct reach j .. j+W-1 is visible
+            first = np.array([j <= i <= j + window - 1 for i in range(n)])
+            assert changed[first].all(), (j, np.nonzero(first & ~changed))
+
+
+@pytest.mark.parametrize("dtype,d,window,chunk", CASES)
+def test_multilayer_cache_slices_hold_each_layers_last_window(dtype, d, window, chunk):
+    t = torch()
+    n_layers, hq, hkv, n = 3, 2, 1, 53
+    weights = make_weights(n_layers, hq, hkv, d, seed=9)
+    x0 = t.randn(n, hq * d, generator=t.Generator(device="cpu").manual_seed(10)).cuda()
+    _, kk, vv, k_rows, v_rows = run_stack(x0, weights, window, chunk, dtype, hq, hkv, d)
+    # one allocation for all layers: L x (Hkv x W x D) elements, W slots per layer whatever n is
+    assert kk.numel() == n_layers * hkv * window * d
+    for layer in range(n_layers):
+        for p in range(n - window, n):
+            assert t.equal(kk[layer, 0, :, p % window].view(t.int16 if dtype == "bf16" else t.int32),
+                           k_rows[layer][p].view(t.int16 if dtype == "bf16" else t.int32)), (layer, p)
+            assert t.equal(vv[layer, 0, :, p % window].view(t.int16 if dtype == "bf16" else t.int32),
+                           v_rows[layer][p].view(t.int16 if dtype == "bf16" else t.int32)), (layer, p)
+    # the layers' K rows differ (independent projections), so a slice mix-up would show
+    assert not t.equal(k_rows[0], k_rows[1])

@@ -150,9 +150,13 @@ def test_figure3_chunks_through_the_ring():
         assert attended == table[i]
 
 
-def test_chunked_through_ring_equals_unchunked():
-    """Chunked prefill through the rolling buffer reproduces unchunked SWA."""
-    rng_seed, n, window, chunk = 31, 1200, 256, 256
+@pytest.mark.parametrize("chunk", [64, 128, 256, 512])
+def test_chunked_through_ring_equals_unchunked(chunk):
+    """Chunked prefill through the rolling buffer reproduces unchunked SWA, for
+    chunks of W/4, W/2, W and 2W (the pages advise chunk = window; a chunk
+    longer than W also applies the window inside itself, and its cache write
+    keeps only the last W tokens)."""
+    rng_seed, n, window = 31, 1200, 256
     hq, hkv, d = 32, 8, 128
     full = make_workload("full", rng_seed, [(0, n), (0, n)], window=window, n_q_heads=hq, n_kv_heads=hkv,
                          head_dim=d, dtype="bf16")
@@ -169,7 +173,7 @@ def test_chunked_through_ring_equals_unchunked():
         swa.swa_prefill_chunk(cache, batch, q[idx].contiguous(), hq, kc, vc, full.scale, qo)
         swa.swa_cache_write(cache, batch, kc, vc)
         out[idx] = qo
-    check_close(host_f32(out, "bf16"), ref, "bf16", "chunked vs unchunked")
+    check_close(host_f32(out, "bf16"), ref, "bf16", f"chunked ({chunk}) vs unchunked")
 
 
 def test_deterministic_bitwise():
