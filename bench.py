@@ -191,6 +191,50 @@ def suite(up, pq, pk, pv, pout, scale, reps: int):
     return res
 
 
+def decode_step_latency(dcache, positions, rows, dq, dk, dv, scale, reps: int, steps_per_graph: int = 16):
+    """Per-token step time for small and full batches (the 64-sequence rings of
+    the main step).  `eager_*`: back-to-back calls from Python, host launch cost
+    included.  `graph_*`: `steps_per_graph` consecutive steps captured in one
+    HIP graph, replay time / steps_per_graph -- the device-side step time.
+    Each form is cache write + decode as two calls, or the fused swa_decode_step."""
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    dev = dq.device
+    res = {}
+    for n in (1, 8, 64):
+        batch = swa.Batch([1] * n, positions[:n], rows[:n])
+        q, k, v = dq[:n], dk[:n], dv[:n]
+        out = torch.empty((n, 32, 128), dtype=torch.bfloat16, device=dev)
+        nb = swa.swa_decode_workspace_size(dcache, n, 32)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+
+        def separate():
+            swa.swa_cache_write(dcache, batch, k, v)
+            swa.swa_decode(dcache, batch, q, 32, scale, out, ws, nb)
+
+        def fused():
+            swa.swa_decode_step(dcache, batch, q, 32, k, v, scale, out, ws, nb)
+
+        rec = {}
+        for name, fn in (("write_then_decode", separate), ("fused_step", fused)):
+            rec["eager_" + name + "_us"] = round(time_ms(fn, reps) * 1e3, 1)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(steps_per_graph):
+                    fn()
+            rec["graph_" + name + "_us"] = round(time_ms(graph.replay, max(2, reps // steps_per_graph)) * 1e3
+                                                 / steps_per_graph, 1)
+            del graph
+        res[f"batch_{n}"] = rec
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +365,8 @@ def main():
     }
     if not args.no_suite:
         result["suite"] = suite(up, pq, pk, pv, pout, wp.scale, reps=10)
+        result["suite"]["decode_step_latency"] = decode_step_latency(
+            dcache, [s.start_pos for s in wd.seqs], list(wd.cache_idx), dq, dk, dv, wd.scale, reps=50)
         result["suite"]["swa_vs_causal_speedup_16k"] = round(
             result["suite"]["causal_prefill_16k"]["ms"] / t_pre, 3)
     if not args.no_cpu_baseline:

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SWA_ABI_VERSION 1
+#define SWA_ABI_VERSION 2  /* 2: swa_decode_step added */
 
 typedef enum swa_dtype {
   SWA_DTYPE_BF16 = 0, /* bfloat16 storage, fp32 arithmetic, bf16 output (round to nearest even) */
@@ -176,6 +176,29 @@ size_t swa_decode_workspace_size(const swa_cache *cache, int32_t num_seqs, int32
 int swa_decode(const swa_cache *cache, const swa_batch *batch,
                const void *q, int32_t n_q_heads, float sm_scale, void *out,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Fused decode step (paragraphs "Rolling Buffer Cache" and "Pre-fill and
+ * Chunking": a generated token's keys and values go to slot pos mod W, and the
+ * token then attends to the window).  Same result as
+ *     swa_cache_write(cache, batch, k_new, v_new, stream);
+ *     swa_decode(cache, batch, q, n_q_heads, sm_scale, out, workspace, workspace_bytes, stream);
+ * -- cache contents and output bit for bit -- in one attention launch (plus the
+ * split-merge launch when the plan splits the window): the new token's K/V
+ * enter the attention directly from k_new / v_new and are written to their
+ * slot by the same launch.  It removes a launch per generated token and, like
+ * every entry point, calls no memset and allocates nothing, so a step can be
+ * captured in a HIP graph and replayed.
+ * k_new, v_new: device [num_seqs][n_kv_heads][head_dim], 16-byte aligned,
+ * NULL rejected.  Batch, q, out and workspace as for swa_decode (the workspace
+ * size is swa_decode_workspace_size()).  Sequences must use distinct cache
+ * rows (checked when h_cache_idx is given).
+ */
+int swa_decode_step(const swa_cache *cache, const swa_batch *batch,
+                    const void *q, int32_t n_q_heads,
+                    const void *k_new, const void *v_new,
+                    float sm_scale, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -93,6 +93,10 @@ def lib():
     L.swa_decode.restype = ctypes.c_int
     L.swa_decode.argtypes = [P(SwaCacheC), P(SwaBatchC), ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.swa_decode_step.restype = ctypes.c_int
+    L.swa_decode_step.argtypes = [P(SwaCacheC), P(SwaBatchC), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p]
     _lib = L
     return L
 
@@ -237,3 +241,15 @@ def swa_decode(cache, batch, q, n_q_heads: int, sm_scale: float, out, workspace=
     code = lib().swa_decode(ctypes.byref(c), ctypes.byref(b), _ptr(q), int(n_q_heads), float(sm_scale), _ptr(out),
                             _ptr(workspace), int(workspace_bytes), _stream(stream))
     return _check(code, "swa_decode") if check else code
+
+
+def swa_decode_step(cache, batch, q, n_q_heads: int, k_new, v_new, sm_scale: float, out, workspace=None,
+                    workspace_bytes=None, stream=None, check: bool = True) -> int:
+    """Fused decode step: writes the new token's K/V into its slot and attends, in one launch."""
+    c, b = _as_cache(cache), _as_batch(batch)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = lib().swa_decode_step(ctypes.byref(c), ctypes.byref(b), _ptr(q), int(n_q_heads), _ptr(k_new),
+                                 _ptr(v_new), float(sm_scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
+                                 _stream(stream))
+    return _check(code, "swa_decode_step") if check else code

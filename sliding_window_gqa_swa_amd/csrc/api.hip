@@ -126,7 +126,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   DecodePlan pl{1, window, 0};
   if (dtype != SWA_DTYPE_BF16 || num_seqs <= 0) return pl;
   // Aim for >= ~2048 workgroups (8 per CU) while keeping >= 256 slots per
-  // workgroup so that each wave streams several 16 KiB steps.
+  // workgroup so that each wave streams several 16 KiB steps.  (Measured for
+  // 1-8 sequences: floors of 128 or 64 slots are slower, the extra partials
+  // cost more than the shorter streams save.)
   const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
   const int64_t target_wg = 2048;
   int64_t max_splits = std::max<int64_t>(1, window / 256);
@@ -138,6 +140,55 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   pl.split_len = (int32_t)len;
   if (splits > 1) pl.workspace_bytes = (size_t)num_seqs * n_q_heads * splits * (head_dim + 2) * sizeof(float);
   return pl;
+}
+
+// swa_decode (k_new == NULL) and swa_decode_step (k_new, v_new given).
+static int decode_impl(const swa_cache *cache, const swa_batch *batch, const void *q, int32_t n_q_heads,
+                       const void *k_new, const void *v_new, float sm_scale, void *out, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const bool fused = k_new != nullptr;
+  swa_status st = check_cache(cache, true);
+  if (st != SWA_OK) return st;
+  st = check_heads(cache, n_q_heads);
+  if (st != SWA_OK) return st;
+  st = check_batch(batch, cache, true, fused);  // the fused step writes: rows must be distinct
+  if (st != SWA_OK) return st;
+  if (!scale_ok(sm_scale)) return SWA_ERR_INVALID_ARGUMENT;
+  if (batch->num_seqs == 0) return SWA_OK;
+  if (!q || !out || !aligned16(q) || !aligned16(out)) return SWA_ERR_INVALID_ARGUMENT;
+  if (fused && (!aligned16(k_new) || !aligned16(v_new))) return SWA_ERR_INVALID_ARGUMENT;
+  const DecodePlan pl = plan_decode(batch->num_seqs, cache->n_kv_heads, n_q_heads, cache->head_dim, cache->window,
+                                    cache->dtype);
+  if (pl.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.workspace_bytes) return SWA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SWA_ERR_INVALID_ARGUMENT;
+  }
+  DecodeParams p{};
+  p.seq = seq_meta(batch, true);
+  p.cache = cache_ref(cache);
+  p.q = q;
+  p.out = out;
+  if (fused) {
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.cache_k_out = cache->k;
+    p.cache_v_out = cache->v;
+  }
+  p.n_q_heads = n_q_heads;
+  p.splits = pl.splits;
+  p.split_len = pl.split_len;
+  p.sm_scale = sm_scale;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  if (pl.workspace_bytes > 0) {
+    p.ws_acc = (float *)workspace;
+    p.ws_ml = p.ws_acc + (size_t)batch->num_seqs * n_q_heads * pl.splits * cache->head_dim;
+  }
+  hipError_t e;
+  if (cache->dtype == SWA_DTYPE_BF16)
+    e = launch_decode_bf16(p, n_q_heads / cache->n_kv_heads, stream);
+  else
+    e = launch_decode_f32(p, stream);
+  return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
 }
 
 }  // namespace swa
@@ -241,41 +292,20 @@ size_t swa_decode_workspace_size(const swa_cache *cache, int32_t num_seqs, int32
 int swa_decode(const swa_cache *cache, const swa_batch *batch, const void *q, int32_t n_q_heads, float sm_scale,
                void *out, void *workspace, size_t workspace_bytes, void *stream) {
   try {
-    swa_status st = check_cache(cache, true);
-    if (st != SWA_OK) return st;
-    st = check_heads(cache, n_q_heads);
-    if (st != SWA_OK) return st;
-    st = check_batch(batch, cache, true, false);
-    if (st != SWA_OK) return st;
-    if (!scale_ok(sm_scale)) return SWA_ERR_INVALID_ARGUMENT;
-    if (batch->num_seqs == 0) return SWA_OK;
-    if (!q || !out || !aligned16(q) || !aligned16(out)) return SWA_ERR_INVALID_ARGUMENT;
-    const DecodePlan pl = plan_decode(batch->num_seqs, cache->n_kv_heads, n_q_heads, cache->head_dim, cache->window,
-                                      cache->dtype);
-    if (pl.workspace_bytes > 0) {
-      if (!workspace || workspace_bytes < pl.workspace_bytes) return SWA_ERR_WORKSPACE;
-      if (!aligned16(workspace)) return SWA_ERR_INVALID_ARGUMENT;
-    }
-    DecodeParams p{};
-    p.seq = seq_meta(batch, true);
-    p.cache = cache_ref(cache);
-    p.q = q;
-    p.out = out;
-    p.n_q_heads = n_q_heads;
-    p.splits = pl.splits;
-    p.split_len = pl.split_len;
-    p.sm_scale = sm_scale;
-    p.scale_log2 = sm_scale * 1.4426950408889634f;
-    if (pl.workspace_bytes > 0) {
-      p.ws_acc = (float *)workspace;
-      p.ws_ml = p.ws_acc + (size_t)batch->num_seqs * n_q_heads * pl.splits * cache->head_dim;
-    }
-    hipError_t e;
-    if (cache->dtype == SWA_DTYPE_BF16)
-      e = launch_decode_bf16(p, n_q_heads / cache->n_kv_heads, (hipStream_t)stream);
-    else
-      e = launch_decode_f32(p, (hipStream_t)stream);
-    return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
+    return decode_impl(cache, batch, q, n_q_heads, nullptr, nullptr, sm_scale, out, workspace, workspace_bytes,
+                       (hipStream_t)stream);
+  } catch (...) {
+    return SWA_ERR_INTERNAL;
+  }
+}
+
+int swa_decode_step(const swa_cache *cache, const swa_batch *batch, const void *q, int32_t n_q_heads,
+                    const void *k_new, const void *v_new, float sm_scale, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  try {
+    if (!k_new || !v_new) return SWA_ERR_INVALID_ARGUMENT;
+    return decode_impl(cache, batch, q, n_q_heads, k_new, v_new, sm_scale, out, workspace, workspace_bytes,
+                       (hipStream_t)stream);
   } catch (...) {
     return SWA_ERR_INTERNAL;
   }

@@ -21,8 +21,12 @@ namespace {
 
 constexpr int kWaves = 4;
 
+// mode: 0 prefill, 1 decode (the new token is already in the ring), 2 fused
+// decode step (the new token comes from k_new / v_new and is written to its
+// slot by the first query head of each KV head)
 template <int D>
-__global__ __launch_bounds__(64 * kWaves) void attend_f32_kernel(PrefillParams p, int decode) {
+__global__ __launch_bounds__(64 * kWaves) void attend_f32_kernel(PrefillParams p, int mode) {
+  const bool decode = mode != 0;
   __shared__ float sq[kWaves][D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_f32_kernel(PrefillParams p
   const int W = p.cache.window;
   // keys below ring_end come from the ring; in decode the query's own key is
   // already there, in prefill the chunk's keys come from k_new / v_new
-  const int ring_end = decode ? s + 1 : s;
+  const int ring_end = mode == 1 ? s + 1 : s;
   const int crow = p.seq.cache_idx ? p.seq.cache_idx[b] : b;
   const float *Q = (const float *)p.q;
   if (active)
@@ -58,6 +62,16 @@ __global__ __launch_bounds__(64 * kWaves) void attend_f32_kernel(PrefillParams p
   const float *ck = (const float *)p.cache.k, *cv = (const float *)p.cache.v;
   const float *kn = (const float *)p.k_new, *vn = (const float *)p.v_new;
   const size_t ring0 = ((size_t)crow * hkv + g) * (size_t)W;
+  if (mode == 2 && h == g * G) {
+    // slot i mod W held position i - W, outside the window of i: nobody reads it here
+    float *wk = (float *)p.cache_k_out + (ring0 + (size_t)(i % W)) * D;
+    float *wv = (float *)p.cache_v_out + (ring0 + (size_t)(i % W)) * D;
+    const size_t off = ((size_t)tok0 * hkv + g) * D;
+    for (int d = lane; d < D; d += 64) {
+      wk[d] = kn[off + d];
+      wv[d] = vn[off + d];
+    }
+  }
   const int lo = max(0, i - W + 1);
   const float cs = p.scale_log2;
 
@@ -117,13 +131,13 @@ __global__ __launch_bounds__(64 * kWaves) void attend_f32_kernel(PrefillParams p
   }
 }
 
-hipError_t launch(const PrefillParams &p, int decode, int max_new, hipStream_t stream) {
+hipError_t launch(const PrefillParams &p, int mode, int max_new, hipStream_t stream) {
   if (p.seq.num_seqs == 0 || max_new == 0) return hipSuccess;
   dim3 grid((unsigned)max_new, (unsigned)p.seq.num_seqs, (unsigned)((p.n_q_heads + kWaves - 1) / kWaves));
   switch (p.cache.head_dim) {
-    case 16: hipLaunchKernelGGL(attend_f32_kernel<16>, grid, dim3(64 * kWaves), 0, stream, p, decode); break;
-    case 64: hipLaunchKernelGGL(attend_f32_kernel<64>, grid, dim3(64 * kWaves), 0, stream, p, decode); break;
-    case 128: hipLaunchKernelGGL(attend_f32_kernel<128>, grid, dim3(64 * kWaves), 0, stream, p, decode); break;
+    case 16: hipLaunchKernelGGL(attend_f32_kernel<16>, grid, dim3(64 * kWaves), 0, stream, p, mode); break;
+    case 64: hipLaunchKernelGGL(attend_f32_kernel<64>, grid, dim3(64 * kWaves), 0, stream, p, mode); break;
+    case 128: hipLaunchKernelGGL(attend_f32_kernel<128>, grid, dim3(64 * kWaves), 0, stream, p, mode); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -144,7 +158,11 @@ hipError_t launch_decode_f32(const DecodeParams &d, hipStream_t stream) {
   p.n_q_heads = d.n_q_heads;
   p.scale_log2 = d.scale_log2;
   p.sm_scale = d.sm_scale;
-  return launch(p, 1, 1, stream);
+  p.k_new = d.k_new;
+  p.v_new = d.v_new;
+  p.cache_k_out = d.cache_k_out;
+  p.cache_v_out = d.cache_v_out;
+  return launch(p, d.k_new ? 2 : 1, 1, stream);
 }
 
 }  // namespace swa

@@ -61,6 +61,22 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
   const uint16_t *kring = (const uint16_t *)p.cache.k + ring0;
   const uint16_t *vring = (const uint16_t *)p.cache.v + ring0;
 
+  // Fused step: the new token (position pos) belongs in slot pos mod W.  The
+  // workgroup whose split holds that slot reads the token's K/V from k_new /
+  // v_new instead of the ring and also writes them there; no other workgroup
+  // of this launch reads the slot, so the result is that of write-then-attend.
+  const bool fused = p.k_new != nullptr;
+  const int new_slot = fused ? pos % W : -1;
+  const uint16_t *knew = fused ? (const uint16_t *)p.k_new + ((size_t)b * hkv + g) * kD : nullptr;
+  const uint16_t *vnew = fused ? (const uint16_t *)p.v_new + ((size_t)b * hkv + g) * kD : nullptr;
+  if (new_slot >= r_begin && new_slot < r_end && wave == 0 && lane < 32) {
+    // 16 lanes copy the 256-byte K row, 16 lanes the V row
+    const int ch = lane & 15;
+    const uint16_t *src = lane < 16 ? knew : vnew;
+    uint16_t *dst = (uint16_t *)(lane < 16 ? p.cache_k_out : p.cache_v_out) + ring0 + (size_t)new_slot * kD;
+    *(u32x4 *)(dst + 8 * ch) = *(const u32x4 *)(src + 8 * ch);
+  }
+
   // query slices of the G heads matching this lane's two 8-element chunks
   u32x4 qa[G], qb[G];
   const uint16_t *Q = (const uint16_t *)p.q;
@@ -90,8 +106,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
       const u32x4 z = {0, 0, 0, 0};
       ka[k] = z; kb[k] = z; va[k] = z; vb[k] = z;
       if (ok[k]) {
-        const uint16_t *kr = kring + (size_t)r * kD;
-        const uint16_t *vr = vring + (size_t)r * kD;
+        const bool is_new = r == new_slot;
+        const uint16_t *kr = is_new ? knew : kring + (size_t)r * kD;
+        const uint16_t *vr = is_new ? vnew : vring + (size_t)r * kD;
         ka[k] = __builtin_nontemporal_load((const u32x4 *)(kr + 8 * c));
         kb[k] = __builtin_nontemporal_load((const u32x4 *)(kr + 64 + 8 * c));
         va[k] = __builtin_nontemporal_load((const u32x4 *)(vr + 8 * c));

@@ -44,6 +44,8 @@ struct PrefillParams {
   const void *k_new;
   const void *v_new;
   void *out;
+  void *cache_k_out;  // fp32 fused decode step only: the writable cache
+  void *cache_v_out;
   int32_t n_q_heads;
   int32_t tiles_per_seq;  // query tiles per sequence (ceil(max_new_tokens / tile))
   int32_t n_work;         // num_seqs * tiles_per_seq * n_kv_heads
@@ -56,6 +58,13 @@ struct DecodeParams {
   CacheRef cache;
   const void *q;
   void *out;
+  // Fused step (write, then attend, in one launch): the new token's K/V rows
+  // [num_seqs][n_kv_heads][head_dim] and the writable cache.  NULL k_new:
+  // plain decode over a cache that already holds the new token.
+  const void *k_new;
+  const void *v_new;
+  void *cache_k_out;
+  void *cache_v_out;
   float *ws_acc;  // [num_seqs][n_q_heads][splits][head_dim]
   float *ws_ml;   // [num_seqs][n_q_heads][splits][2]  (max in log2 units, sum)
   int32_t n_q_heads;

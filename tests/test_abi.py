@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["swa_abi_version", "swa_status_string", "swa_cache_write", "swa_prefill_chunk",
-                            "swa_decode_workspace_size", "swa_decode"])
+                            "swa_decode_workspace_size", "swa_decode", "swa_decode_step"])
     lib = swa.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     text = open(HEADER).read()
-    assert swa.swa_abi_version() == int(re.search(r"#define SWA_ABI_VERSION (\d+)", text).group(1))
+    assert swa.swa_abi_version() == int(re.search(r"#define SWA_ABI_VERSION (\d+)", text).group(1)) == 2
     for code in range(6):
         s = swa.swa_status_string(code)
         assert s and isinstance(s, str)
@@ -79,6 +79,10 @@ def decode(c, b, hq=32, scale=0.088, ws=None, wsb=0, q=FAKE, out=FAKE):
     return swa.swa_decode(c, b.c, q, hq, scale, out, ws, wsb, stream=0, check=False)
 
 
+def step(c, b, hq=32, scale=0.088, ws=None, wsb=0, q=FAKE, kn=FAKE, vn=FAKE, out=FAKE):
+    return swa.swa_decode_step(c, b.c, q, hq, kn, vn, scale, out, ws, wsb, stream=0, check=False)
+
+
 INVALID, UNSUPPORTED, WORKSPACE = swa.SWA_ERR_INVALID_ARGUMENT, swa.SWA_ERR_UNSUPPORTED, swa.SWA_ERR_WORKSPACE
 
 
@@ -88,6 +92,7 @@ def test_null_structs_are_rejected():
     assert lib.swa_cache_write(None, ctypes.byref(b.c), FAKE, FAKE, None) == INVALID
     assert lib.swa_prefill_chunk(ctypes.byref(cache()), None, FAKE, 32, FAKE, FAKE, 0.1, FAKE, None) == INVALID
     assert lib.swa_decode(None, None, FAKE, 32, 0.1, FAKE, None, 0, None) == INVALID
+    assert lib.swa_decode_step(None, None, FAKE, 32, FAKE, FAKE, 0.1, FAKE, None, 0, None) == INVALID
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -151,6 +156,25 @@ def test_decode_argument_checks():
     assert decode(c, one, hq=33, ws=FAKE, wsb=need) == INVALID
     assert decode(c, one, scale=float("inf"), ws=FAKE, wsb=need) == INVALID
     assert decode(cache(v=None), one, ws=FAKE, wsb=need) == INVALID
+
+
+def test_decode_step_argument_checks():
+    c = cache(window=4096)
+    one = HostBatch([1, 1], [5, 9])
+    need = swa.swa_decode_workspace_size(c, 2, 32)
+    # everything swa_decode rejects ...
+    assert step(c, HostBatch([2, 1], [5, 9]), ws=FAKE, wsb=need) == INVALID
+    assert step(c, one, ws=None, wsb=0) == WORKSPACE
+    assert step(c, one, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert step(c, one, hq=33, ws=FAKE, wsb=need) == INVALID
+    assert step(c, one, scale=0.0, ws=FAKE, wsb=need) == INVALID
+    assert step(cache(v=None, window=4096), one, ws=FAKE, wsb=need) == INVALID
+    # ... plus the new token's rows and the write's distinct-row rule
+    assert step(c, one, kn=None, ws=FAKE, wsb=need) == INVALID
+    assert step(c, one, vn=None, ws=FAKE, wsb=need) == INVALID
+    assert step(c, one, kn=FAKE + 8, ws=FAKE, wsb=need) == INVALID
+    assert step(c, HostBatch([1, 1], [5, 9], rows=[3, 3]), ws=FAKE, wsb=need) == INVALID
+    assert step(c, HostBatch([], [])) == swa.SWA_OK
 
 
 def test_workspace_plan():

@@ -1,0 +1,139 @@
+"""GPU checks of swa_decode_step, the fused decode step.
+
+Mistral 7B (Chinese translation), section 2, paragraphs "Rolling Buffer Cache"
+and "Pre-fill and Chunking": a generated token's keys and values are stored in
+slot pos mod W, then the token attends to the window.  swa_decode_step does
+both in one launch, so it must reproduce swa_cache_write followed by
+swa_decode bit for bit (outputs and cache contents), and match the fp64 oracle
+within the usual tolerance.  A step is also captured in a HIP graph and
+replayed with new tokens and advanced positions.
+"""
+import numpy as np
+import pytest
+
+import sliding_window_gqa_swa_amd as swa
+from sliding_window_gqa_swa_amd.workloads import batched_decode, make_workload
+from helpers import check_close, dev, host_f32, host_raw, oracle_all, poisoned_cache, torch, write_history
+
+pytestmark = pytest.mark.gpu
+
+
+def clone_cache(c):
+    return swa.Cache(c.k.clone(), c.v.clone())
+
+
+def workspace(cache, n, hq):
+    nb = swa.swa_decode_workspace_size(cache, n, hq)
+    return torch().empty(max(nb, 16), dtype=torch().uint8, device="cuda"), nb
+
+
+def separate_and_fused(wl, cache):
+    """Run write + decode on one copy of the cache and the fused step on another."""
+    t = torch()
+    c_sep, c_fus = clone_cache(cache), clone_cache(cache)
+    batch = swa.Batch([1] * wl.num_seqs, [s.start_pos for s in wl.seqs], wl.cache_idx)
+    q, kn, vn = dev(wl.q, wl.dtype), dev(wl.k_new, wl.dtype), dev(wl.v_new, wl.dtype)
+    ws, nb = workspace(cache, wl.num_seqs, wl.n_q_heads)
+    dt = t.bfloat16 if wl.dtype == "bf16" else t.float32
+    o_sep = t.full((wl.num_seqs, wl.n_q_heads, wl.head_dim), float("nan"), dtype=dt, device="cuda")
+    o_fus = t.full_like(o_sep, float("nan"))
+    swa.swa_cache_write(c_sep, batch, kn, vn)
+    swa.swa_decode(c_sep, batch, q, wl.n_q_heads, wl.scale, o_sep, ws, nb)
+    swa.swa_decode_step(c_fus, batch, q, wl.n_q_heads, kn, vn, wl.scale, o_fus, ws, nb)
+    t.cuda.synchronize()
+    return (c_sep, o_sep), (c_fus, o_fus)
+
+
+def assert_same_bits(a, b, what):
+    t = torch()
+    iv = t.int16 if a.dtype == t.bfloat16 else t.int32
+    assert t.equal(a.view(iv), b.view(iv)), what
+
+
+@pytest.mark.parametrize("dtype,window,group", [("bf16", 4096, 4), ("bf16", 100, 8), ("bf16", 1, 1),
+                                                ("bf16", 300, 2), ("f32", 64, 4), ("f32", 5, 1)])
+def test_fused_step_equals_write_then_decode(dtype, window, group):
+    hkv = 2
+    d = 128 if dtype == "bf16" else 16
+    positions = sorted({0, 1, max(0, window - 2), window - 1, window, window + 1, 3 * window + 5, 9000})
+    wl = make_workload("step", 70 + window, [(p, 1) for p in positions], window=window, n_q_heads=hkv * group,
+                       n_kv_heads=hkv, head_dim=d, dtype=dtype, cache_rows=list(reversed(range(len(positions)))))
+    cache = poisoned_cache(wl.n_cache, hkv, window, d, dtype)
+    write_history(cache, wl)
+    (c_sep, o_sep), (c_fus, o_fus) = separate_and_fused(wl, cache)
+    assert_same_bits(o_sep, o_fus, "output")
+    assert_same_bits(c_sep.k, c_fus.k, "cache K")
+    assert_same_bits(c_sep.v, c_fus.v, "cache V")
+    check_close(host_f32(o_fus, dtype), oracle_all(wl), dtype, f"fused step W={window}")
+
+
+def test_fused_step_full_size_batched_decode():
+    """64 sequences at positions in [4096, 32768), full 4096-slot rings (split plan with workspace)."""
+    wl = batched_decode(1004)
+    cache = poisoned_cache(64, 8, 4096, 128, "bf16")
+    write_history(cache, wl)
+    (c_sep, o_sep), (c_fus, o_fus) = separate_and_fused(wl, cache)
+    assert_same_bits(o_sep, o_fus, "output")
+    assert_same_bits(c_sep.k, c_fus.k, "cache K")
+    assert_same_bits(c_sep.v, c_fus.v, "cache V")
+    check_close(host_f32(o_fus, "bf16"), oracle_all(wl), "bf16", "fused step, batched decode")
+
+
+def test_graph_captured_step_replays_match_eager_steps():
+    """Capture one fused step (split plan, with workspace), then replay it for
+    several generated tokens: between replays the inputs are refilled and the
+    device positions advance.  Every replay must equal the same step run
+    eagerly on a second cache, output and cache bit for bit."""
+    t = torch()
+    n, hq, hkv, d, window = 4, 32, 8, 128, 4096
+    rng = np.random.default_rng(123)
+    start = [5000, 4096, 4200, 12345]
+    wl = make_workload("graph", 124, [(p, 1) for p in start], window=window, n_q_heads=hq, n_kv_heads=hkv,
+                       head_dim=d, dtype="bf16")
+    cache_g = poisoned_cache(n, hkv, window, d, "bf16")
+    write_history(cache_g, wl)
+    cache_e = clone_cache(cache_g)
+
+    batch_g = swa.Batch([1] * n, start, list(range(n)))
+    batch_e = swa.Batch([1] * n, start, list(range(n)))
+    q = t.empty((n, hq, d), dtype=t.bfloat16, device="cuda")
+    kn = t.empty((n, hkv, d), dtype=t.bfloat16, device="cuda")
+    vn = t.empty((n, hkv, d), dtype=t.bfloat16, device="cuda")
+    out_g = t.empty((n, hq, d), dtype=t.bfloat16, device="cuda")
+    out_e = t.empty_like(out_g)
+    ws_g, nb = workspace(cache_g, n, hq)
+    ws_e, _ = workspace(cache_g, n, hq)
+    assert nb > 0
+
+    def refill():
+        q.copy_(t.from_numpy(rng.standard_normal((n, hq, d), dtype=np.float32)).to(t.bfloat16))
+        kn.copy_(t.from_numpy(rng.standard_normal((n, hkv, d), dtype=np.float32)).to(t.bfloat16))
+        vn.copy_(t.from_numpy(rng.standard_normal((n, hkv, d), dtype=np.float32)).to(t.bfloat16))
+
+    refill()
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):  # warm-up launch outside the capture, on a scratch cache
+        scratch = clone_cache(cache_g)
+        swa.swa_decode_step(scratch, batch_g, q, hq, kn, vn, wl.scale, out_g, ws_g, nb)
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    del scratch
+
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.graph(graph):
+        swa.swa_decode_step(cache_g, batch_g, q, hq, kn, vn, wl.scale, out_g, ws_g, nb)
+    for step in range(5):
+        if step > 0:
+            refill()
+            batch_g.sp.add_(1)
+            batch_e.sp.add_(1)
+            batch_e.h_sp += 1
+        graph.replay()
+        t.cuda.synchronize()
+        swa.swa_decode_step(cache_e, batch_e, q, hq, kn, vn, wl.scale, out_e, ws_e, nb)
+        t.cuda.synchronize()
+        assert_same_bits(out_g, out_e, f"replay {step}: output")
+        assert_same_bits(cache_g.k, cache_e.k, f"replay {step}: cache K")
+        assert_same_bits(cache_g.v, cache_e.v, f"replay {step}: cache V")
+        assert not t.isnan(out_g.float()).any()
