@@ -37,7 +37,9 @@
 //     rows are loaded from the nearest key of the band (always written data)
 //     and masked, so unwritten cache slots cannot reach the arithmetic.
 //   * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
-//   * Workgroups are ordered heaviest-first and mapped XCD-contiguously.
+//   * Work order (KV head, sequence, query tile from the last), dealt to the
+//     XCDs in contiguous ranges: one KV head per XCD balances ragged batches
+//     and keeps each head's K/V in one L2.
 #include "device_common.h"
 #include "swa_internal.h"
 
@@ -74,12 +76,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave choices scalar
+  // Work order (KV head, sequence, query tile from the last), dealt to the XCDs
+  // in contiguous ranges: with 8 KV heads every XCD takes one head of every
+  // sequence -- the same share of a ragged batch -- and only that head's K/V
+  // passes through its L2; the workgroups resident on an XCD at a time work on
+  // neighbouring query tiles of one sequence, whose windows overlap.
   const int work = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, p.n_work));
   const int tps = p.tiles_per_seq;
-  const int qt = tps - 1 - (work % tps);  // heaviest (latest) query tile first
-  const int bg = work / tps;
+  const int nseq = p.seq.num_seqs;
   const int hkv = p.cache.n_kv_heads;
-  const int g = __builtin_amdgcn_readfirstlane(bg % hkv), b = __builtin_amdgcn_readfirstlane(bg / hkv);
+  const int g = __builtin_amdgcn_readfirstlane(work / (nseq * tps));
+  const int rem = work % (nseq * tps);
+  const int b = __builtin_amdgcn_readfirstlane(rem / tps);
+  const int qt = __builtin_amdgcn_readfirstlane(tps - 1 - rem % tps);  // heaviest (latest) first
 
   // workgroup-uniform metadata (kept in scalar registers)
   const int tok0 = __builtin_amdgcn_readfirstlane(p.seq.cu_seqlens[b]);
