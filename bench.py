@@ -249,7 +249,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the multi-GPU sharding of this path is described in DESIGN.md but not built.", file=sys.stderr)
+              "the path would shard by sequence or KV head (decode) and by query range with a\n"
+              "W-1 position halo (prefill), but no multi-GPU code is built.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
