@@ -92,6 +92,23 @@ def time_ms(fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def time_ms_cold(fn, reps: int, flush) -> float:
+    """Mean milliseconds of `fn`, each launch timed alone after `flush` has
+    overwritten the 256 MB Infinity Cache (so no input is served from it)."""
+    import torch
+    fn()
+    total = 0.0
+    for _ in range(reps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    return total / reps
+
+
 def suite(up, pq, pk, pv, pout, scale, reps: int):
     """The other workloads of the path, timed (their parity is covered by the GPU tests)."""
     import numpy as np
@@ -150,6 +167,13 @@ def suite(up, pq, pk, pv, pout, scale, reps: int):
                             "activation_mib_per_call": round(act / 2**20, 1)}
         del ob
     res["chunk_sweep_4x32k_w4096"] = sweep
+    # the same chunk write with a cold Infinity Cache: 512 MiB written before each launch
+    big = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    batch = swa.Batch([C] * B, [N - C] * B, list(range(B)))
+    kc = kd[:, N - C:].reshape(B * C, 8, 128).contiguous()
+    vc = vd[:, N - C:].reshape(B * C, 8, 128).contiguous()
+    t_w_cold = time_ms_cold(lambda: swa.swa_cache_write(cache, batch, kc, vc), reps, lambda: big.fill_(1))
+    del big, kc, vc
     del qd, kd, vd
     tot_ms = sum(c[0] for c in chunks)
     tot_fl = sum(c[2] for c in chunks)
@@ -159,7 +183,9 @@ def suite(up, pq, pk, pv, pout, scale, reps: int):
         "prefill_tflops_chunks_1_7": round(sum(c[2] for c in chunks[1:]) / sum(c[0] for c in chunks[1:]) / 1e9, 1),
         "prefill_tflops_all": round(tot_fl / tot_ms / 1e9, 1),
         "cache_write_ms_per_chunk": round(float(np.mean([c[1] for c in chunks])), 4),
-        "cache_write_gbps": round(wbytes / float(np.mean([c[1] for c in chunks])) / 1e6, 1)}
+        "cache_write_gbps": round(wbytes / float(np.mean([c[1] for c in chunks])) / 1e6, 1),
+        "cache_write_cold_ms": round(t_w_cold, 4),
+        "cache_write_cold_gbps": round(wbytes / t_w_cold / 1e6, 1)}
     del cache
 
     # ragged mixed batch: 16 prefill + 32 decode sequences sharing one 48-row cache
