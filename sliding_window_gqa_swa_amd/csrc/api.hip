@@ -127,8 +127,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   if (dtype != SWA_DTYPE_BF16 || num_seqs <= 0) return pl;
   // Aim for >= ~2048 workgroups (8 per CU) while keeping >= 256 slots per
   // workgroup so that each wave streams several 16 KiB steps.  (Measured for
-  // 1-8 sequences: floors of 128 or 64 slots are slower, the extra partials
-  // cost more than the shorter streams save.)
+  // 1-8 sequences: floors of 128 or 64 slots are slower.)
   const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
   const int64_t target_wg = 2048;
   int64_t max_splits = std::max<int64_t>(1, window / 256);

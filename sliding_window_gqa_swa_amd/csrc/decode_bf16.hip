@@ -215,21 +215,40 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
   }
 }
 
-// Merge the per-split partials of each (sequence, query head).
+// Merge the per-split partials of each (sequence, query head).  The partials
+// are read kBatch at a time (independent loads in flight together); the sums
+// still run in split order.  An empty split (max -inf) has weight 0.
 __global__ __launch_bounds__(kD) void decode_combine_bf16_kernel(DecodeParams p) {
+  constexpr int kBatch = 8;
   const int bh = blockIdx.x, d = threadIdx.x;
   const int S = p.splits;
   const float *ml = p.ws_ml + (size_t)bh * S * 2;
   const float *acc = p.ws_acc + (size_t)bh * S * kD;
   float mx = -INFINITY;
-  for (int s = 0; s < S; s++) mx = fmaxf(mx, ml[2 * s]);
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float mv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) mv[i] = s0 + i < S ? ml[2 * (s0 + i)] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) mx = fmaxf(mx, mv[i]);
+  }
   float ls = 0.f, os = 0.f;
-  for (int s = 0; s < S; s++) {
-    const float ms = ml[2 * s];
-    if (ms == -INFINITY) continue;  // empty split
-    const float f = exp2f(ms - mx);
-    ls += ml[2 * s + 1] * f;
-    os += acc[(size_t)s * kD + d] * f;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float mv[kBatch], lv[kBatch], av[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) {
+      const bool in = s0 + i < S;
+      mv[i] = in ? ml[2 * (s0 + i)] : -INFINITY;
+      lv[i] = in ? ml[2 * (s0 + i) + 1] : 0.f;
+      av[i] = in ? acc[(size_t)(s0 + i) * kD + d] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) {
+      if (mv[i] == -INFINITY) continue;  // empty split or past the end
+      const float f = exp2f(mv[i] - mx);
+      ls += lv[i] * f;
+      os += av[i] * f;
+    }
   }
   ((uint16_t *)p.out)[(size_t)bh * kD + d] = (uint16_t)pack_bf16(os / ls, 0.f);
 }
