@@ -348,11 +348,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     softmax(kt0 + t * kBN, masked);
     wait_vmem();
     __syncthreads();
+    // the matrix half-step's wave issues first when both waves of the SIMD are
+    // ready (MFMAs and operand reads ahead of the other wave's softmax VALU)
+    __builtin_amdgcn_s_setprio(3);
     pv(vslot(t & 1));
     if constexpr (decltype(with_qk)::value) {
       qk(kslot((t + 1) % 3));
       schedule_matrix_half_step();
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   };
 
