@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SWA-GQA prefill band-TFLOP/s + decode KV GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+SPEC_CLOCK_GHZ = 2.4        # the clock the MFMA peak is quoted at
 PREFILL_KERNEL = "prefill_bf16_kernel"
 PMC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_mistral16k_w4096_pmc.json")
 PREFILL_SRC = os.path.join(ROOT, "sliding_window_gqa_swa_amd", "csrc", "prefill_bf16.hip")
@@ -47,16 +48,36 @@ def src_digest(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def pmc_traffic(launches_per_step: int = 1):
-    """HBM bytes per prefill launch from the committed counter summary, or None
-    when it is missing or the kernel source changed since it was taken."""
+def pmc_record():
+    """The committed counter summary of the prefill kernel, or None when it is
+    missing or the kernel source changed since the counters were taken."""
     try:
         rec = json.load(open(PMC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_src_sha") != src_digest(PREFILL_SRC):
         return None
-    return float(rec["traffic_bytes_per_launch"])
+    return rec
+
+
+def pmc_traffic():
+    """HBM bytes per prefill launch (calibrated FETCH_SIZE + WRITE_SIZE), or None."""
+    rec = pmc_record()
+    return None if rec is None else float(rec["traffic_bytes_per_launch"])
+
+
+def sclk_estimate(t_launch_ms: float, tflops: float):
+    """Shader clock implied by the prefill's cycle count per launch (GRBM_GUI_ACTIVE
+    per XCD, constant from launch to launch) and its measured duration, with the
+    fraction of the MFMA peak at that clock; None without the counter summary."""
+    rec = pmc_record()
+    if rec is None or "cycles_per_xcd_per_launch" not in rec:
+        return None
+    ghz = float(rec["cycles_per_xcd_per_launch"]) / (t_launch_ms * 1e6)
+    peak_at_clk = PEAK_BF16_TFLOPS * ghz / SPEC_CLOCK_GHZ
+    return {"ghz": round(ghz, 3), "spec_ghz": SPEC_CLOCK_GHZ, "mfma_peak_at_sclk_tflops": round(peak_at_clk, 1),
+            "frac_of_peak_at_sclk": round(tflops / peak_at_clk, 4),
+            "source": "GRBM_GUI_ACTIVE cycles per launch / 8 XCDs / the launch's measured duration"}
 
 
 def cpu_baseline(wl, sample_rows: int):
@@ -359,6 +380,7 @@ def main():
     dec_gbps = kv_bytes / (t_dec * 1e-3) / 1e9
 
     traffic = pmc_traffic()
+    sclk = sclk_estimate(t_pre, tflops)
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -382,6 +404,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": PREFILL_KERNEL, "algorithmic_flops_per_launch": band_flops},
+        "sclk": sclk,
         "decode_roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                             "algorithmic_bytes_per_launch": kv_bytes},
