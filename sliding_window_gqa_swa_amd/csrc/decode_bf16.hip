@@ -36,11 +36,19 @@ constexpr int kRowsPerStep = 32;
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
-  __shared__ float sm_acc[kWaves][G][kD];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
+  // A wave serves at most 4 query heads (registers: accumulators and query
+  // slices grow with the heads).  With G = 8 the waves split into two head
+  // groups of 4; both groups stream every row of the split (the second read of
+  // a row is served by the caches).
+  constexpr int GW = G < 4 ? G : 4;          // query heads per wave
+  constexpr int NHG = G / GW;                // head groups
+  constexpr int kRowWaves = kWaves / NHG;    // waves streaming the rows for one head group
+  __shared__ float sm_acc[kRowWaves][G][kD];
+  __shared__ float sm_m[kRowWaves][G];
+  __shared__ float sm_l[kRowWaves][G];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = wave % NHG, rw = wave / NHG;
   const int grp = lane >> 3, c = lane & 7;
   const int splits = p.splits;
   const int sp = blockIdx.x % splits;
@@ -77,26 +85,26 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
     *(u32x4 *)(dst + 8 * ch) = *(const u32x4 *)(src + 8 * ch);
   }
 
-  // query slices of the G heads matching this lane's two 8-element chunks
-  u32x4 qa[G], qb[G];
+  // query slices of this wave's GW heads matching this lane's two 8-element chunks
+  u32x4 qa[GW], qb[GW];
   const uint16_t *Q = (const uint16_t *)p.q;
 #pragma unroll
-  for (int hh = 0; hh < G; hh++) {
-    const uint16_t *qrow = Q + ((size_t)b * hq + g * G + hh) * kD;
+  for (int hh = 0; hh < GW; hh++) {
+    const uint16_t *qrow = Q + ((size_t)b * hq + g * G + hg * GW + hh) * kD;
     qa[hh] = *(const u32x4 *)(qrow + 8 * c);
     qb[hh] = *(const u32x4 *)(qrow + 64 + 8 * c);
   }
 
-  float m[G], l[G], acc[G][16];
+  float m[GW], l[GW], acc[GW][16];
 #pragma unroll
-  for (int hh = 0; hh < G; hh++) {
+  for (int hh = 0; hh < GW; hh++) {
     m[hh] = -INFINITY;
     l[hh] = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e++) acc[hh][e] = 0.f;
   }
 
-  for (int r0 = r_begin + kRowsPerStep * wave; r0 < r_end; r0 += kRowsPerStep * kWaves) {
+  for (int r0 = r_begin + kRowsPerStep * rw; r0 < r_end; r0 += kRowsPerStep * kRowWaves) {
     u32x4 ka[4], kb[4], va[4], vb[4];
     bool ok[4];
 #pragma unroll
@@ -115,11 +123,11 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
         vb[k] = __builtin_nontemporal_load((const u32x4 *)(vr + 64 + 8 * c));
       }
     }
-    float sc[G][4];
+    float sc[GW][4];
 #pragma unroll
     for (int k = 0; k < 4; k++)
 #pragma unroll
-      for (int hh = 0; hh < G; hh++) {
+      for (int hh = 0; hh < GW; hh++) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; e++) d = fdot2_bf16(ka[k][e], qa[hh][e], d);
@@ -128,9 +136,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
         d = sum8(d);
         sc[hh][k] = ok[k] ? d * cs : -INFINITY;
       }
-    float pk[G][4];
+    float pk[GW][4];
 #pragma unroll
-    for (int hh = 0; hh < G; hh++) {
+    for (int hh = 0; hh < GW; hh++) {
       float mb = fmaxf(fmaxf(sc[hh][0], sc[hh][1]), fmaxf(sc[hh][2], sc[hh][3]));
       mb = max_over_groups8(mb);  // row r0 is valid, so mb is finite
       const float mn = fmaxf(m[hh], mb);
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
         vf[8 + 2 * e + 1] = bf16hi(vb[k][e]);
       }
 #pragma unroll
-      for (int hh = 0; hh < G; hh++)
+      for (int hh = 0; hh < GW; hh++)
 #pragma unroll
         for (int e = 0; e < 16; e++) acc[hh][e] = __builtin_fmaf(pk[hh][k], vf[e], acc[hh][e]);
     }
@@ -166,22 +174,23 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
 
   // combine the 8 lane groups of the wave (they share m), then the waves
 #pragma unroll
-  for (int hh = 0; hh < G; hh++) {
+  for (int hh = 0; hh < GW; hh++) {
     l[hh] = sum_over_groups8(l[hh]);
 #pragma unroll
     for (int e = 0; e < 16; e++) acc[hh][e] = sum_over_groups8(acc[hh][e]);
   }
   if (grp == 0) {
 #pragma unroll
-    for (int hh = 0; hh < G; hh++) {
+    for (int hh = 0; hh < GW; hh++) {
+      const int hw = hg * GW + hh;  // head index within the group of G
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        sm_acc[wave][hh][8 * c + e] = acc[hh][e];
-        sm_acc[wave][hh][64 + 8 * c + e] = acc[hh][8 + e];
+        sm_acc[rw][hw][8 * c + e] = acc[hh][e];
+        sm_acc[rw][hw][64 + 8 * c + e] = acc[hh][8 + e];
       }
       if (c == 0) {
-        sm_m[wave][hh] = m[hh];
-        sm_l[wave][hh] = l[hh];
+        sm_m[rw][hw] = m[hh];
+        sm_l[rw][hw] = l[hh];
       }
     }
   }
@@ -191,11 +200,11 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
     const int hh = idx / kD, d = idx % kD;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) mx = fmaxf(mx, sm_m[w][hh]);
+    for (int w = 0; w < kRowWaves; w++) mx = fmaxf(mx, sm_m[w][hh]);
     float ls = 0.f, os = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; w++) {
+      for (int w = 0; w < kRowWaves; w++) {
         const float f = exp2f(sm_m[w][hh] - mx);
         ls += sm_l[w][hh] * f;
         os += sm_acc[w][hh][d] * f;
