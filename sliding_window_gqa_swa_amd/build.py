@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libswa.so")
-SOURCES = ["api.hip", "cache_write.hip", "prefill_bf16.hip", "decode_bf16.hip", "attend_f32.hip"]
+SOURCES = ["api.hip", "cache_write.hip", "prefill_bf16.hip", "decode_bf16.hip", "decode_mfma.hip", "attend_f32.hip"]
 ARCH = "gfx950"
 
 

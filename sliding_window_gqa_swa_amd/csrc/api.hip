@@ -121,15 +121,21 @@ static swa_status check_heads(const swa_cache *c, int32_t n_q_heads) {
 
 static bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
+// bf16 decode with G >= 2 query heads per KV head runs on the matrix cores
+// (decode_mfma.hip); G = 1 on the VALU kernel (decode_bf16.hip).
+constexpr int kMfmaMinGroup = 2;
+
 DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, int32_t head_dim, int32_t window,
                        int32_t dtype) {
   DecodePlan pl{1, window, 0};
   if (dtype != SWA_DTYPE_BF16 || num_seqs <= 0) return pl;
-  // Aim for >= ~2048 workgroups (8 per CU) while keeping >= 256 slots per
-  // workgroup so that each wave streams several 16 KiB steps.  (Measured for
-  // 1-8 sequences: floors of 128 or 64 slots are slower.)
+  // Workgroups per launch to aim for.  The VALU kernel (G = 1) wants >= ~2048
+  // (8 per CU).  The matrix-core kernel (G >= 2) holds 2 workgroups per CU, so
+  // 512 fill the chip once: 64 sequences x 8 KV heads then take one split per
+  // ring and need no merge launch.  A split keeps >= 256 slots either way, so
+  // that each wave streams several 16 KiB steps.
   const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
-  const int64_t target_wg = 2048;
+  const int64_t target_wg = n_q_heads / n_kv_heads >= kMfmaMinGroup ? 512 : 2048;
   int64_t max_splits = std::max<int64_t>(1, window / 256);
   int64_t splits = std::min<int64_t>(max_splits, std::max<int64_t>(1, (target_wg + pairs - 1) / pairs));
   int64_t len = (window + splits - 1) / splits;
@@ -183,8 +189,10 @@ static int decode_impl(const swa_cache *cache, const swa_batch *batch, const voi
     p.ws_ml = p.ws_acc + (size_t)batch->num_seqs * n_q_heads * pl.splits * cache->head_dim;
   }
   hipError_t e;
+  const int group = n_q_heads / cache->n_kv_heads;
   if (cache->dtype == SWA_DTYPE_BF16)
-    e = launch_decode_bf16(p, n_q_heads / cache->n_kv_heads, stream);
+    e = group >= kMfmaMinGroup ? launch_decode_mfma_bf16(p, group, stream)
+                                        : launch_decode_bf16(p, group, stream);
   else
     e = launch_decode_f32(p, stream);
   return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;

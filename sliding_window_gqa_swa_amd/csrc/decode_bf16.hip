@@ -12,6 +12,11 @@
 // positions max(0, pos-W+1) .. pos, so the query attends to every valid slot;
 // softmax attention is a sum over keys and needs no slot -> position map.
 //
+// The library launches this kernel for G = 1 only; G = 2, 4, 8 run on the
+// matrix cores (decode_mfma.hip), because the per-head VALU work here grows
+// with G.  The template still handles G <= 8, and the split merge (combine
+// kernel) below serves both kernels.
+//
 // Design (HBM-bound: 4 FLOP per byte of K/V):
 //   * One workgroup = (sequence, KV head, split of the window): 4 waves.  All
 //     G query heads are served from the same loaded K/V rows (GQA sharing).
@@ -266,24 +271,24 @@ template <int G>
 hipError_t launch_g(const DecodeParams &p, hipStream_t stream) {
   const unsigned n_wg = (unsigned)p.seq.num_seqs * p.cache.n_kv_heads * p.splits;
   hipLaunchKernelGGL(decode_bf16_kernel<G>, dim3(n_wg), dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(decode_combine_bf16_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads), dim3(kD), 0,
-                     stream, p);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode_combine_bf16(p, stream);
 }
 
 }  // namespace
 
+hipError_t launch_decode_combine_bf16(const DecodeParams &p, hipStream_t stream) {
+  if (p.seq.num_seqs == 0 || p.splits == 1) return hipSuccess;
+  hipLaunchKernelGGL(decode_combine_bf16_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads), dim3(kD), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_bf16(const DecodeParams &p, int group, hipStream_t stream) {
   if (p.seq.num_seqs == 0) return hipSuccess;
-  switch (group) {
-    case 1: return launch_g<1>(p, stream);
-    case 2: return launch_g<2>(p, stream);
-    case 4: return launch_g<4>(p, stream);
-    case 8: return launch_g<8>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (group != 1) return hipErrorInvalidValue;
+  return launch_g<1>(p, stream);
 }
 
 }  // namespace swa

@@ -87,7 +87,9 @@ hipError_t launch_cache_write(const CacheWriteParams &p, hipStream_t stream);
 int prefill_bf16_tile_rows(int group);
 hipError_t launch_prefill_bf16(const PrefillParams &p, int group, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream);
-hipError_t launch_decode_bf16(const DecodeParams &p, int group, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams &p, int group, hipStream_t stream);       // group 1
+hipError_t launch_decode_mfma_bf16(const DecodeParams &p, int group, hipStream_t stream);  // group 2, 4, 8
+hipError_t launch_decode_combine_bf16(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream);
 
 }  // namespace swa

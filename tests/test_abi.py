@@ -179,9 +179,14 @@ def test_decode_step_argument_checks():
 
 def test_workspace_plan():
     c = cache(window=4096, n_cache=64)
-    sz = swa.swa_decode_workspace_size(c, 64, 32)
-    # 64 sequences x 8 KV heads: the window is split; workspace = B x Hq x splits x (D + 2) floats
-    assert sz > 0 and sz % (64 * 32 * (128 + 2) * 4) == 0
+    # 64 sequences x 8 KV heads (G = 4): 512 workgroups fill the chip, one split per ring
+    assert swa.swa_decode_workspace_size(c, 64, 32) == 0
+    # 8 sequences: the window is split; workspace = B x Hq x splits x (D + 2) floats
+    sz = swa.swa_decode_workspace_size(c, 8, 32)
+    assert sz > 0 and sz % (8 * 32 * (128 + 2) * 4) == 0
+    # G = 1 (32 KV heads) aims at more workgroups: 16 sequences already split
+    sz1 = swa.swa_decode_workspace_size(cache(window=4096, n_cache=64, n_kv_heads=32), 16, 32)
+    assert sz1 > 0 and sz1 % (16 * 32 * (128 + 2) * 4) == 0
     assert swa.swa_decode_workspace_size(c, 0, 32) == 0
     assert swa.swa_decode_workspace_size(cache(window=64), 2, 32) == 0      # too short to split
     assert swa.swa_decode_workspace_size(cache(dtype=swa.SWA_DTYPE_F32), 2, 32) == 0

@@ -51,10 +51,12 @@ def test_window_one_is_exact():
         assert np.array_equal(got[:, h, :], wl.v_new[:, h // 4, :])
 
 
-def test_full_size_batched_decode():
-    """64 sequences at positions in [4096, 32768), full 4096-slot rings, 32 q / 8 kv heads."""
-    wl = batched_decode(1004)
-    cache = poisoned_cache(64, 8, 4096, 128, "bf16")
+@pytest.mark.parametrize("batch", [64, 8])
+def test_full_size_batched_decode(batch):
+    """Sequences at positions in [4096, 32768), full 4096-slot rings, 32 q / 8 kv heads.
+    64 sequences take one workgroup per ring; 8 sequences split each window (workspace and merge)."""
+    wl = batched_decode(1004, batch=batch)
+    cache = poisoned_cache(batch, 8, 4096, 128, "bf16")
     write_history(cache, wl)
     got = host_f32(run_decode(wl, cache), "bf16")
     check_close(got, oracle_all(wl), "bf16", "batched decode")

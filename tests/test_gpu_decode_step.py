@@ -67,10 +67,12 @@ def test_fused_step_equals_write_then_decode(dtype, window, group):
     check_close(host_f32(o_fus, dtype), oracle_all(wl), dtype, f"fused step W={window}")
 
 
-def test_fused_step_full_size_batched_decode():
-    """64 sequences at positions in [4096, 32768), full 4096-slot rings (split plan with workspace)."""
-    wl = batched_decode(1004)
-    cache = poisoned_cache(64, 8, 4096, 128, "bf16")
+@pytest.mark.parametrize("batch", [64, 8])
+def test_fused_step_full_size_batched_decode(batch):
+    """Sequences at positions in [4096, 32768), full 4096-slot rings: 64 sequences (one
+    workgroup per ring) and 8 (split windows, workspace and merge)."""
+    wl = batched_decode(1004, batch=batch)
+    cache = poisoned_cache(batch, 8, 4096, 128, "bf16")
     write_history(cache, wl)
     (c_sep, o_sep), (c_fus, o_fus) = separate_and_fused(wl, cache)
     assert_same_bits(o_sep, o_fus, "output")
