@@ -19,18 +19,18 @@
 //     global_load_lds (XOR-swizzled 16-byte chunks) and come back transposed
 //     with ds_read_b64_tr_b16; P^T stays in registers (the S^T accumulator
 //     layout is the B-operand layout).
-//   * The next step's K (registers) and V (the other LDS buffer) are in flight
-//     while a step is computed.  The two V buffers are distinct LDS objects and
-//     the loop is unrolled by two, so the compiler can tell a buffer being
-//     filled from the one being read and does not wait for the prefetch.
+//   * Two K register sets and two V buffers: once a step has its scores, the
+//     next step's K (registers) and V (the other LDS buffer) are issued and
+//     stay in flight through this step's softmax and P V.  The two V buffers
+//     are distinct LDS objects and the loop is unrolled by two, so the
+//     compiler can tell a buffer being filled from the one being read and
+//     does not wait for the prefetch before reading.
 //   * Keys past the split (a partial last step) read the split's last valid
 //     row and are masked to -inf: unwritten slots are never read.
 //   * Waves merge through LDS (log-sum-exp), splits through the workspace and
 //     the combine kernel of decode_bf16.hip.
 #include "device_common.h"
 #include "swa_internal.h"
-
-#include <type_traits>
 
 namespace swa {
 namespace {
