@@ -62,6 +62,21 @@ def test_full_size_batched_decode(batch):
     check_close(got, oracle_all(wl), "bf16", "batched decode")
 
 
+@pytest.mark.parametrize("group,batch", [(2, 16), (8, 16), (8, 64)])
+def test_full_size_group_sizes(group, batch):
+    """Full 4096-slot rings at the other group sizes of the matrix-core kernel: 32 query heads over
+    32 / G KV heads.  (2, 16): 2 splits per ring; (8, 16): 8 splits; (8, 64): 2 splits."""
+    hkv = 32 // group
+    pos = np.random.default_rng(1100 + group + batch).integers(4096, 32768, size=batch)
+    wl = make_workload(f"groups-{group}-{batch}", 1200 + group + batch, [(int(p), 1) for p in pos], window=4096,
+                       n_q_heads=32, n_kv_heads=hkv, head_dim=128, dtype="bf16")
+    cache = poisoned_cache(batch, hkv, 4096, 128, "bf16")
+    write_history(cache, wl)
+    assert swa.swa_decode_workspace_size(cache, batch, 32) > 0
+    got = host_f32(run_decode(wl, cache), "bf16")
+    check_close(got, oracle_all(wl), "bf16", f"decode G={group} B={batch}")
+
+
 def test_many_short_sequences_single_split_plan():
     # enough (sequence, head) pairs that the plan uses no workspace
     positions = list(np.random.default_rng(2).integers(0, 300, size=300))
