@@ -43,6 +43,13 @@
 #include "device_common.h"
 #include "swa_internal.h"
 
+#ifndef PREFILL_QSCALE
+#define PREFILL_QSCALE 1
+#endif
+#ifndef PREFILL_MFMA_ROWSUM
+#define PREFILL_MFMA_ROWSUM 1
+#endif
+
 #include <type_traits>
 
 namespace swa {
@@ -125,6 +132,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     for (int ks = 0; ks < 4; ks++) {
       u32x4 v = {0, 0, 0, 0};
       if (ok) v = *(const u32x4 *)(qrow + 32 * ks);
+#if PREFILL_QSCALE
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        v[e] = pack_bf16(__builtin_bit_cast(float, v[e] << 16) * c, __builtin_bit_cast(float, v[e] & 0xFFFF0000u) * c);
+#endif
       qf[ks][qb] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -201,8 +213,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY};  // running max, log2 units
+#if PREFILL_MFMA_ROWSUM
+  // row sums on the matrix cores: lsum[qb] += 1 P^T, so every register of a
+  // lane holds the whole sum of its query column (no cross-lane reduction)
+  f32x4 lsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair});
+#else
   float l[2] = {0.f, 0.f};              // this lane's share of the row sums
+#endif
   f32x4 sa[4][2];                       // S^T of the tile in flight: 4 key blocks x 2 query blocks
+#if PREFILL_QSCALE
+  f32x4 negm[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // accumulator start: -m (0 while m = -inf)
+  float gap[2] = {-INFINITY, -INFINITY};  // rescale threshold on the tile max of the accumulators
+#endif
   u32x4 pw[2][2];                       // P^T (bf16 pairs) of the softmaxed tile: [32-key slice][qb]
 
   // S^T = K Q^T (the order of LDS reads and MFMAs is set by the half-step schedule)
@@ -210,7 +233,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
     for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
+#if PREFILL_QSCALE
+      for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = negm[qb];
+#else
       for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#endif
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
@@ -248,6 +275,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         o[db][0] = mfma16(vf, p0, o[db][0]);
         o[db][1] = mfma16(vf, p1, o[db][1]);
       }
+#if PREFILL_MFMA_ROWSUM
+      lsum[0] = mfma16(ones, p0, lsum[0]);
+      lsum[1] = mfma16(ones, p1, lsum[1]);
+#endif
     }
   };
 
@@ -271,6 +302,46 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             if ((unsigned)(d0 + 16 * kbi + i) >= (unsigned)W) sa[kbi][qb][i] = -INFINITY;
       }
     }
+#if PREFILL_QSCALE
+    // sa already holds score * scale * log2 e - mc (Q was scaled, the
+    // accumulators started at negm = -mc), where mc is the running max m when
+    // this tile's scores were computed, or 0 while m = -inf.  The tile needs a
+    // rescale iff its max exceeds m by more than the slack, i.e. iff
+    // max(sa) > gap with gap = kRescaleSlack (m finite) or -inf (m = -inf).
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+      // tile max of this lane's 16 values as a chain of 3-input maxima
+      float mt = fmaxf(sa[0][qb][0], sa[0][qb][1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2)
+        mt = fmaxf(fmaxf(mt, sa[e / 4][qb][e % 4]), sa[e / 4][qb][e % 4 + 1]);
+      mt = max_pair32(max_pair16(mt));
+      const bool upd = mt > gap[qb];
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        const bool m_inf = gap[qb] == -INFINITY;
+        const float mc = -negm[qb][0];
+        const float mn = upd ? mt + mc : (m_inf ? -INFINITY : mc);
+        const float alpha = m_inf ? 0.f : __builtin_amdgcn_exp2f(mc - mn);
+#if PREFILL_MFMA_ROWSUM
+        lsum[qb] *= alpha;
+#else
+        l[qb] *= alpha;
+#endif
+#pragma unroll
+        for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
+        const bool mn_inf = mn == -INFINITY;
+        const float shift = mn_inf ? 0.f : mn - mc;  // 0 where m did not move
+#pragma unroll
+        for (int kbi = 0; kbi < 4; kbi++) sa[kbi][qb] -= shift;
+        const float nm = mn_inf ? 0.f : -mn;
+        negm[qb] = f32x4{nm, nm, nm, nm};
+        gap[qb] = mn_inf ? -INFINITY : kRescaleSlack;
+      }
+#pragma unroll
+      for (int kbi = 0; kbi < 4; kbi++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(sa[kbi][qb][i]);
+#else
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
       float mt = -INFINITY;
@@ -284,7 +355,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         const float mn = upd ? mts : m[qb];
         const float alpha = (m[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[qb] - mn);
         m[qb] = mn;
+#if PREFILL_MFMA_ROWSUM
+        lsum[qb] *= alpha;
+#else
         l[qb] *= alpha;
+#endif
 #pragma unroll
         for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
       }
@@ -293,6 +368,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
         for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kbi][qb][i], c, -mc));
+#endif
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
         u32x4 w;
@@ -301,9 +377,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         w[2] = pack_bf16(sa[2 * kk + 1][qb][0], sa[2 * kk + 1][qb][1]);
         w[3] = pack_bf16(sa[2 * kk + 1][qb][2], sa[2 * kk + 1][qb][3]);
         pw[kk][qb] = w;
+#if !PREFILL_MFMA_ROWSUM
         // row sum of the bf16-rounded weights, i.e. of exactly what enters P V
 #pragma unroll
         for (int e = 0; e < 4; e++) l[qb] = fdot2_bf16(w[e], kBf16OnePair, l[qb]);
+#endif
       }
     }
   };
@@ -339,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // 0x008: MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 64 - 2 * kPairs, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 64 + 4 * PREFILL_MFMA_ROWSUM - 2 * kPairs, 0);
   };
 
   auto step = [&](int t, bool masked, auto with_qk) __attribute__((always_inline)) {
@@ -385,8 +463,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   uint16_t *O = (uint16_t *)p.out;
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
+#if PREFILL_MFMA_ROWSUM
+    const float lt = lsum[qb][0];
+#else
     float lt = l[qb];
     lt = add_pair32(add_pair16(lt));
+#endif
     const float inv = 1.0f / lt;
     const int qrel = qoff + 16 * qb + (lane & 15);
     if (qrel < n_rows) {
