@@ -36,19 +36,21 @@
 //     mask code.  Keys outside the band are never read from outside it: their
 //     rows are loaded from the nearest key of the band (always written data)
 //     and masked, so unwritten cache slots cannot reach the arithmetic.
-//   * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA).
+//   * Online softmax in fp32 with exp2.  The softmax half-step competes with
+//     the other wave's MFMAs for the VALU issue port, so its instruction count
+//     per tile bounds the matrix rate; it is kept small:
+//       - Q is multiplied by scale * log2 e once (rounded to bf16) and the
+//         score accumulators start at -m, so a weight is exp2 of the
+//         accumulator, with no FMA per score;
+//       - the row sums are an MFMA of the bf16 weights with a ones operand,
+//         which also leaves every lane with its query's complete sum;
+//       - the rescale test is one compare of the tile max against a per-row
+//         threshold.
 //   * Work order (KV head, sequence, query tile from the last), dealt to the
 //     XCDs in contiguous ranges: one KV head per XCD balances ragged batches
 //     and keeps each head's K/V in one L2.
 #include "device_common.h"
 #include "swa_internal.h"
-
-#ifndef PREFILL_QSCALE
-#define PREFILL_QSCALE 1
-#endif
-#ifndef PREFILL_MFMA_ROWSUM
-#define PREFILL_MFMA_ROWSUM 1
-#endif
 
 #include <type_traits>
 
@@ -132,11 +134,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     for (int ks = 0; ks < 4; ks++) {
       u32x4 v = {0, 0, 0, 0};
       if (ok) v = *(const u32x4 *)(qrow + 32 * ks);
-#if PREFILL_QSCALE
+      // q * scale * log2 e, rounded to bf16: scores come out in log2 units
 #pragma unroll
       for (int e = 0; e < 4; e++)
         v[e] = pack_bf16(__builtin_bit_cast(float, v[e] << 16) * c, __builtin_bit_cast(float, v[e] & 0xFFFF0000u) * c);
-#endif
       qf[ks][qb] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -212,32 +213,25 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   for (int db = 0; db < 8; db++)
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};  // running max, log2 units
-#if PREFILL_MFMA_ROWSUM
-  // row sums on the matrix cores: lsum[qb] += 1 P^T, so every register of a
-  // lane holds the whole sum of its query column (no cross-lane reduction)
+  // Running max m of each query row (log2 units), kept as the accumulator
+  // start negm = -m (0 while m = -inf) and the rescale threshold gap
+  // (kRescaleSlack while m is finite, -inf before).
+  f32x4 negm[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float gap[2] = {-INFINITY, -INFINITY};
+  // Row sums on the matrix cores: lsum[qb] += ones P^T, so every register of a
+  // lane holds the whole sum of its query column (no cross-lane reduction).
   f32x4 lsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair});
-#else
-  float l[2] = {0.f, 0.f};              // this lane's share of the row sums
-#endif
   f32x4 sa[4][2];                       // S^T of the tile in flight: 4 key blocks x 2 query blocks
-#if PREFILL_QSCALE
-  f32x4 negm[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // accumulator start: -m (0 while m = -inf)
-  float gap[2] = {-INFINITY, -INFINITY};  // rescale threshold on the tile max of the accumulators
-#endif
   u32x4 pw[2][2];                       // P^T (bf16 pairs) of the softmaxed tile: [32-key slice][qb]
 
-  // S^T = K Q^T (the order of LDS reads and MFMAs is set by the half-step schedule)
+  // S^T - m = K Q^T + negm (the order of LDS reads and MFMAs is set by the
+  // half-step schedule)
   auto qk = [&](const unsigned char *kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
-#if PREFILL_QSCALE
       for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = negm[qb];
-#else
-      for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#endif
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
@@ -263,8 +257,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     return __builtin_bit_cast(bf16x8, w);
   };
 
-  // O^T += V^T P^T (order of reads and MFMAs as for qk)
+  // row sums and O^T += V^T P^T (order of reads and MFMAs as for qk)
   auto pv = [&](const unsigned char *vbase) __attribute__((always_inline)) {
+    // row sums of exactly the bf16 weights that enter P V; these MFMAs need no
+    // LDS data, so they go first, under the latency of the first operand reads
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      lsum[0] = mfma16(ones, __builtin_bit_cast(bf16x8, pw[kk][0]), lsum[0]);
+      lsum[1] = mfma16(ones, __builtin_bit_cast(bf16x8, pw[kk][1]), lsum[1]);
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) {
       const bf16x8 p0 = __builtin_bit_cast(bf16x8, pw[kk][0]);
@@ -275,19 +276,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         o[db][0] = mfma16(vf, p0, o[db][0]);
         o[db][1] = mfma16(vf, p1, o[db][1]);
       }
-#if PREFILL_MFMA_ROWSUM
-      lsum[0] = mfma16(ones, p0, lsum[0]);
-      lsum[1] = mfma16(ones, p1, lsum[1]);
-#endif
     }
   };
 
-  // mask (edge tiles), online softmax, P^T as bf16 into pw, row sums.
+  // mask (edge tiles), online softmax, P^T as bf16 into pw.
   // A query's 64 keys sit in lanes l, l^16, l^32, l^48.  The running max m is
   // kept in log2 units (score * scale * log2 e) and only moves when a tile's
   // max exceeds it by more than kRescaleSlack: the weights then stay
-  // <= 2^kRescaleSlack, O/l are rescaled only on those (rare) tiles, and the
-  // result is unchanged because O and l share m.
+  // <= 2^kRescaleSlack, O and the row sums are rescaled only on those (rare)
+  // tiles, and the result is unchanged because they share m.
   auto softmax = [&](int ts, bool masked) __attribute__((always_inline)) {
     if (masked) {
       __asm__ volatile("");  // keep this a branch: only edge tiles pay for the mask
@@ -302,7 +299,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             if ((unsigned)(d0 + 16 * kbi + i) >= (unsigned)W) sa[kbi][qb][i] = -INFINITY;
       }
     }
-#if PREFILL_QSCALE
     // sa already holds score * scale * log2 e - mc (Q was scaled, the
     // accumulators started at negm = -mc), where mc is the running max m when
     // this tile's scores were computed, or 0 while m = -inf.  The tile needs a
@@ -322,11 +318,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         const float mc = -negm[qb][0];
         const float mn = upd ? mt + mc : (m_inf ? -INFINITY : mc);
         const float alpha = m_inf ? 0.f : __builtin_amdgcn_exp2f(mc - mn);
-#if PREFILL_MFMA_ROWSUM
         lsum[qb] *= alpha;
-#else
-        l[qb] *= alpha;
-#endif
 #pragma unroll
         for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
         const bool mn_inf = mn == -INFINITY;
@@ -341,34 +333,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
         for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(sa[kbi][qb][i]);
-#else
-#pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kbi = 0; kbi < 4; kbi++)
-        mt = fmaxf(mt, fmaxf(fmaxf(sa[kbi][qb][0], sa[kbi][qb][1]), fmaxf(sa[kbi][qb][2], sa[kbi][qb][3])));
-      mt = max_pair32(max_pair16(mt));
-      const float mts = mt * c;
-      const bool upd = mts > m[qb] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(upd)) {
-        const float mn = upd ? mts : m[qb];
-        const float alpha = (m[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[qb] - mn);
-        m[qb] = mn;
-#if PREFILL_MFMA_ROWSUM
-        lsum[qb] *= alpha;
-#else
-        l[qb] *= alpha;
-#endif
-#pragma unroll
-        for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
-      }
-      const float mc = (m[qb] == -INFINITY) ? 0.f : m[qb];
-#pragma unroll
-      for (int kbi = 0; kbi < 4; kbi++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kbi][qb][i], c, -mc));
-#endif
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
         u32x4 w;
@@ -377,11 +341,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         w[2] = pack_bf16(sa[2 * kk + 1][qb][0], sa[2 * kk + 1][qb][1]);
         w[3] = pack_bf16(sa[2 * kk + 1][qb][2], sa[2 * kk + 1][qb][3]);
         pw[kk][qb] = w;
-#if !PREFILL_MFMA_ROWSUM
-        // row sum of the bf16-rounded weights, i.e. of exactly what enters P V
-#pragma unroll
-        for (int e = 0; e < 4; e++) l[qb] = fdot2_bf16(w[e], kBf16OnePair, l[qb]);
-#endif
       }
     }
   };
@@ -403,21 +362,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int n_diag_free = (q0 - kBN + 1 - kt0) >= 0 ? (q0 - kBN + 1 - kt0) / kBN + 1 : 0;
   const int t_mid_end = max(n_lead, min(n_tiles, n_diag_free));
 
-  // Order of the matrix half-step's 48 LDS reads (32 V, then 16 K) and 64
-  // MFMAs (32 PV, then 32 QK): eight reads first, then two MFMAs and two reads
-  // alternately, so reads run about four MFMA pairs ahead of their consumers
-  // and the K reads of the next QK overlap the tail of PV.  (The compiler may
+  // Order of the matrix half-step's 48 LDS reads (32 V, then 16 K) and 68
+  // MFMAs (4 row sums, 32 PV, then 32 QK): eight reads first, then the four
+  // row-sum MFMAs, then two MFMAs and two reads alternately, so reads run
+  // about four MFMA pairs ahead of their consumers and the K reads of the next
+  // QK overlap the tail of PV.  (The compiler may
   // still move the last QK MFMAs past the closing barrier; measured, that
   // beats keeping them inside.)
   auto schedule_matrix_half_step = [&]() __attribute__((always_inline)) {
     constexpr int kReads = 48, kLead = 8, kPairs = (kReads - kLead) / 2;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // 0x100: LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // the row-sum MFMAs
 #pragma unroll
     for (int i = 0; i < kPairs; i++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // 0x008: MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 64 + 4 * PREFILL_MFMA_ROWSUM - 2 * kPairs, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 64 - 2 * kPairs, 0);
   };
 
   auto step = [&](int t, bool masked, auto with_qk) __attribute__((always_inline)) {
@@ -463,12 +424,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   uint16_t *O = (uint16_t *)p.out;
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
-#if PREFILL_MFMA_ROWSUM
     const float lt = lsum[qb][0];
-#else
-    float lt = l[qb];
-    lt = add_pair32(add_pair16(lt));
-#endif
     const float inv = 1.0f / lt;
     const int qrel = qoff + 16 * qb + (lane & 15);
     if (qrel < n_rows) {
