@@ -39,9 +39,8 @@
 //   * Online softmax in fp32 with exp2.  The softmax half-step competes with
 //     the other wave's MFMAs for the VALU issue port, so its instruction count
 //     per tile bounds the matrix rate; it is kept small:
-//       - Q is multiplied by scale * log2 e once (rounded to bf16) and the
-//         score accumulators start at -m, so a weight is exp2 of the
-//         accumulator, with no FMA per score;
+//       - the score accumulators start at -M (the running max of q.k), so
+//         a weight is exp2(c * accumulator), one multiply per score;
 //       - the row sums are an MFMA of the bf16 weights with a ones operand,
 //         which also leaves every lane with its query's complete sum;
 //       - the rescale test is one compare of the tile max against a per-row
@@ -134,10 +133,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     for (int ks = 0; ks < 4; ks++) {
       u32x4 v = {0, 0, 0, 0};
       if (ok) v = *(const u32x4 *)(qrow + 32 * ks);
-      // q * scale * log2 e, rounded to bf16: scores come out in log2 units
-#pragma unroll
-      for (int e = 0; e < 4; e++)
-        v[e] = pack_bf16(__builtin_bit_cast(float, v[e] << 16) * c, __builtin_bit_cast(float, v[e] & 0xFFFF0000u) * c);
       qf[ks][qb] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -213,11 +208,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   for (int db = 0; db < 8; db++)
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Running max m of each query row (log2 units), kept as the accumulator
-  // start negm = -m (0 while m = -inf) and the rescale threshold gap
-  // (kRescaleSlack while m is finite, -inf before).
+  // Running max M of each query row's raw scores q.k, kept as the accumulator
+  // start negm = -M (0 while M = -inf) and the rescale threshold gap on the
+  // tile max of the accumulators (kRescaleSlack / c while M is finite, -inf
+  // before).
   f32x4 negm[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float gap[2] = {-INFINITY, -INFINITY};
+  const float gap_finite = kRescaleSlack / c;
   // Row sums on the matrix cores: lsum[qb] += ones P^T, so every register of a
   // lane holds the whole sum of its query column (no cross-lane reduction).
   f32x4 lsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -225,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   f32x4 sa[4][2];                       // S^T of the tile in flight: 4 key blocks x 2 query blocks
   u32x4 pw[2][2];                       // P^T (bf16 pairs) of the softmaxed tile: [32-key slice][qb]
 
-  // S^T - m = K Q^T + negm (the order of LDS reads and MFMAs is set by the
+  // S^T - M = K Q^T + negm (the order of LDS reads and MFMAs is set by the
   // half-step schedule)
   auto qk = [&](const unsigned char *kb) __attribute__((always_inline)) {
 #pragma unroll
@@ -280,11 +277,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   };
 
   // mask (edge tiles), online softmax, P^T as bf16 into pw.
-  // A query's 64 keys sit in lanes l, l^16, l^32, l^48.  The running max m is
-  // kept in log2 units (score * scale * log2 e) and only moves when a tile's
-  // max exceeds it by more than kRescaleSlack: the weights then stay
-  // <= 2^kRescaleSlack, O and the row sums are rescaled only on those (rare)
-  // tiles, and the result is unchanged because they share m.
+  // A query's 64 keys sit in lanes l, l^16, l^32, l^48.  The running max M
+  // only moves when a tile's max exceeds it by more than kRescaleSlack in log2
+  // units (c (q.k - M)): the weights then stay <= 2^kRescaleSlack, O and the
+  // row sums are rescaled only on those (rare) tiles, and the result is
+  // unchanged because they share M.
   auto softmax = [&](int ts, bool masked) __attribute__((always_inline)) {
     if (masked) {
       __asm__ volatile("");  // keep this a branch: only edge tiles pay for the mask
@@ -299,11 +296,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             if ((unsigned)(d0 + 16 * kbi + i) >= (unsigned)W) sa[kbi][qb][i] = -INFINITY;
       }
     }
-    // sa already holds score * scale * log2 e - mc (Q was scaled, the
-    // accumulators started at negm = -mc), where mc is the running max m when
-    // this tile's scores were computed, or 0 while m = -inf.  The tile needs a
-    // rescale iff its max exceeds m by more than the slack, i.e. iff
-    // max(sa) > gap with gap = kRescaleSlack (m finite) or -inf (m = -inf).
+    // sa already holds q.k - mc (the accumulators started at negm = -mc),
+    // where mc is the running max M when this tile's scores were computed, or
+    // 0 while M = -inf.  The weight of a key is exp2(c (q.k - M)).  The tile
+    // needs a rescale iff its max exceeds M by more than kRescaleSlack / c,
+    // i.e. iff max(sa) > gap.
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
       // tile max of this lane's 16 values as a chain of 3-input maxima
@@ -317,22 +314,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         const bool m_inf = gap[qb] == -INFINITY;
         const float mc = -negm[qb][0];
         const float mn = upd ? mt + mc : (m_inf ? -INFINITY : mc);
-        const float alpha = m_inf ? 0.f : __builtin_amdgcn_exp2f(mc - mn);
+        const float alpha = m_inf ? 0.f : __builtin_amdgcn_exp2f((mc - mn) * c);
         lsum[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
         const bool mn_inf = mn == -INFINITY;
-        const float shift = mn_inf ? 0.f : mn - mc;  // 0 where m did not move
+        const float shift = mn_inf ? 0.f : mn - mc;  // 0 where M did not move
 #pragma unroll
         for (int kbi = 0; kbi < 4; kbi++) sa[kbi][qb] -= shift;
         const float nm = mn_inf ? 0.f : -mn;
         negm[qb] = f32x4{nm, nm, nm, nm};
-        gap[qb] = mn_inf ? -INFINITY : kRescaleSlack;
+        gap[qb] = mn_inf ? -INFINITY : gap_finite;
       }
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(sa[kbi][qb][i]);
+        for (int i = 0; i < 4; i++) sa[kbi][qb][i] = __builtin_amdgcn_exp2f(sa[kbi][qb][i] * c);
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
         u32x4 w;
