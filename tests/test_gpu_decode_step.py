@@ -81,6 +81,22 @@ def test_fused_step_full_size_batched_decode(batch):
     check_close(host_f32(o_fus, "bf16"), oracle_all(wl), "bf16", "fused step, batched decode")
 
 
+@pytest.mark.parametrize("group", [2, 8])
+def test_fused_step_full_size_group_sizes(group):
+    """16 sequences, full 4096-slot rings, 32 query heads over 32 / G KV heads (split plans)."""
+    hkv = 32 // group
+    pos = np.random.default_rng(1300 + group).integers(4096, 32768, size=16)
+    wl = make_workload(f"step-g{group}", 1400 + group, [(int(p), 1) for p in pos], window=4096, n_q_heads=32,
+                       n_kv_heads=hkv, head_dim=128, dtype="bf16")
+    cache = poisoned_cache(16, hkv, 4096, 128, "bf16")
+    write_history(cache, wl)
+    (c_sep, o_sep), (c_fus, o_fus) = separate_and_fused(wl, cache)
+    assert_same_bits(o_sep, o_fus, "output")
+    assert_same_bits(c_sep.k, c_fus.k, "cache K")
+    assert_same_bits(c_sep.v, c_fus.v, "cache V")
+    check_close(host_f32(o_fus, "bf16"), oracle_all(wl), "bf16", f"fused step G={group}")
+
+
 def test_graph_captured_step_replays_match_eager_steps():
     """Capture one fused step (split plan, with workspace), then replay it for
     several generated tokens: between replays the inputs are refilled and the
