@@ -66,8 +66,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
   const int pos = p.seq.start_pos[b];
   const int n_valid = min(pos + 1, W);
   const int crow = p.seq.cache_idx ? p.seq.cache_idx[b] : b;
-  const int r_begin = sp * p.split_len;
-  const int r_end = min(r_begin + p.split_len, n_valid);
+  const int len = seq_split_len(n_valid, splits, p.split_len);
+  const int r_begin = sp * len;
+  const int r_end = min(r_begin + len, n_valid);
   const float cs = p.scale_log2;
 
   const size_t ring0 = ((size_t)crow * hkv + g) * (size_t)W * kD;

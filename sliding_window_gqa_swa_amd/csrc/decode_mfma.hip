@@ -84,8 +84,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int n_valid = min(pos + 1, W);
   const int crow = p.seq.cache_idx ? __builtin_amdgcn_readfirstlane(p.seq.cache_idx[b]) : b;
   // uniform by construction; readfirstlane lets the compiler branch on them with scalar branches
-  const int r_begin = __builtin_amdgcn_readfirstlane(sp * p.split_len);
-  const int r_end = __builtin_amdgcn_readfirstlane(min(r_begin + p.split_len, n_valid));
+  const int len = __builtin_amdgcn_readfirstlane(seq_split_len(n_valid, splits, p.split_len));
+  const int r_begin = __builtin_amdgcn_readfirstlane(sp * len);
+  const int r_end = __builtin_amdgcn_readfirstlane(min(r_begin + len, n_valid));
   const float c = p.scale_log2;
 
   const size_t ring0 = ((size_t)crow * hkv + g) * (size_t)W * kD;

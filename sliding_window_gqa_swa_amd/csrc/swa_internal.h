@@ -69,10 +69,23 @@ struct DecodeParams {
   float *ws_ml;   // [num_seqs][n_q_heads][splits][2]  (max in log2 units, sum)
   int32_t n_q_heads;
   int32_t splits;
-  int32_t split_len;  // slots per split
+  int32_t split_len;  // slots per split for a full window (see seq_split_len)
   float scale_log2;
   float sm_scale;
 };
+
+// Slots per split of one sequence in a decode launch.  The plan fixes the
+// number of splits and a split length that covers the whole window; a
+// sequence with fewer valid slots spreads them evenly over all its splits
+// instead (multiples of 32, at least kMinSplitRows), so a short context still
+// runs on every split.  splits * result >= n_valid always holds.
+constexpr int kMinSplitRows = 128;
+__device__ __forceinline__ int seq_split_len(int n_valid, int splits, int plan_len) {
+  int len = (n_valid + splits - 1) / splits;
+  len = (len + 31) & ~31;
+  len = len > kMinSplitRows ? len : kMinSplitRows;
+  return len < plan_len ? len : plan_len;
+}
 
 // Decode plan: how the window of each (sequence, KV head) is split across workgroups.
 struct DecodePlan {
