@@ -97,15 +97,17 @@ def test_fused_step_full_size_group_sizes(group):
     check_close(host_f32(o_fus, "bf16"), oracle_all(wl), "bf16", f"fused step G={group}")
 
 
-def test_graph_captured_step_replays_match_eager_steps():
+@pytest.mark.parametrize("start", [[5000, 4096, 4200, 12345], [2044, 100, 2047, 3000]])
+def test_graph_captured_step_replays_match_eager_steps(start):
     """Capture one fused step (split plan, with workspace), then replay it for
     several generated tokens: between replays the inputs are refilled and the
     device positions advance.  Every replay must equal the same step run
-    eagerly on a second cache, output and cache bit for bit."""
+    eagerly on a second cache, output and cache bit for bit.  The second set of
+    positions starts below W: two sequences cross 2048 valid slots while the
+    graph replays, which changes how their slots are spread over the splits."""
     t = torch()
     n, hq, hkv, d, window = 4, 32, 8, 128, 4096
     rng = np.random.default_rng(123)
-    start = [5000, 4096, 4200, 12345]
     wl = make_workload("graph", 124, [(p, 1) for p in start], window=window, n_q_heads=hq, n_kv_heads=hkv,
                        head_dim=d, dtype="bf16")
     cache_g = poisoned_cache(n, hkv, window, d, "bf16")
