@@ -240,16 +240,18 @@ def suite(up, pq, pk, pv, pout, scale, reps: int):
 
 def decode_step_latency(dcache, positions, rows, dq, dk, dv, scale, reps: int, steps_per_graph: int = 16):
     """Per-token step time for small and full batches (the 64-sequence rings of
-    the main step).  `eager_*`: back-to-back calls from Python, host launch cost
-    included.  `graph_*`: `steps_per_graph` consecutive steps captured in one
-    HIP graph, replay time / steps_per_graph -- the device-side step time.
-    Each form is cache write + decode as two calls, or the fused swa_decode_step."""
+    the main step, full windows), and for 1 and 8 sequences at position 500
+    (a context shorter than the window).  `eager_*`: back-to-back calls from
+    Python, host launch cost included.  `graph_*`: `steps_per_graph`
+    consecutive steps captured in one HIP graph, replay time / steps_per_graph
+    -- the device-side step time.  Each form is cache write + decode as two
+    calls, or the fused swa_decode_step."""
     import torch
     import sliding_window_gqa_swa_amd as swa
     dev = dq.device
     res = {}
-    for n in (1, 8, 64):
-        batch = swa.Batch([1] * n, positions[:n], rows[:n])
+    for n, short in ((1, False), (8, False), (64, False), (1, True), (8, True)):
+        batch = swa.Batch([1] * n, [500] * n if short else positions[:n], rows[:n])
         q, k, v = dq[:n], dk[:n], dv[:n]
         out = torch.empty((n, 32, 128), dtype=torch.bfloat16, device=dev)
         nb = swa.swa_decode_workspace_size(dcache, n, 32)
@@ -278,7 +280,7 @@ def decode_step_latency(dcache, positions, rows, dq, dk, dv, scale, reps: int, s
             rec["graph_" + name + "_us"] = round(time_ms(graph.replay, max(2, reps // steps_per_graph)) * 1e3
                                                  / steps_per_graph, 1)
             del graph
-        res[f"batch_{n}"] = rec
+        res[f"batch_{n}" + ("_pos500" if short else "")] = rec
     return res
 
 
