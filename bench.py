@@ -230,10 +230,18 @@ def suite(up, pq, pk, pv, pout, scale, reps: int):
         t_d = time_ms(lambda: swa.swa_decode(cache, db, dq, 32, scale, do, ws, wsb), reps)
         pfl = 4.0 * 128 * 32 * sum(band_pairs(s.start_pos, s.n_new, W) for s in wp.seqs)
         kvb = sum(2 * 8 * 128 * 2 * min(s.start_pos + 1, W) for s in wd.seqs)
+        # roofline bound of each launch: its algorithmic FLOPs or bytes at the
+        # MFMA / HBM peak, and the end-to-end time of the three launches
+        # against the sum of their bounds
+        wbytes = 2 * 2 * wd.num_seqs * 8 * 128 * 2
+        b_p, b_d, b_w = pfl / (PEAK_BF16_TFLOPS * 1e9), kvb / (PEAK_HBM_GBPS * 1e6), wbytes / (PEAK_HBM_GBPS * 1e6)
         res["mixed_" + ("ctx8192" if variant else "loguniform")] = {
             "prefill_ms": round(t_p, 4), "prefill_tflops": round(pfl / t_p / 1e9, 1),
             "decode_us": round(t_d * 1e3, 1), "decode_gbps": round(kvb / t_d / 1e6, 1),
-            "decode_write_us": round(t_dw * 1e3, 1)}
+            "decode_write_us": round(t_dw * 1e3, 1),
+            "bound_ms": {"prefill": round(b_p, 4), "decode": round(b_d, 4), "decode_write": round(b_w, 5)},
+            "end_to_end_ms": round(t_p + t_d + t_dw, 4),
+            "end_to_end_frac_of_bound": round((b_p + b_d + b_w) / (t_p + t_d + t_dw), 3)}
         del cache
     return res
 
