@@ -94,7 +94,16 @@ def cpu_baseline(wl, sample_rows: int):
     oracle.attend(q, rows, k, v, 0, wl.window, wl.scale)
     dt = time.perf_counter() - t0
     flops = 4.0 * wl.head_dim * wl.n_q_heads * sum(min(int(i) + 1, wl.window) for i in rows)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"{len(rows)} of the {n} query rows (evenly spaced) x {wl.n_q_heads} heads of the "
                       f"16384-token prefill (W={wl.window}), fp64, {flops / 1e9:.1f} GFLOP in {dt:.2f} s"}
 
@@ -431,6 +440,7 @@ def main():
             result["suite"]["causal_prefill_16k"]["ms"] / t_pre, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wp, args.cpu_sample_rows)
+        result["cpu_baseline"]["gpu_over_cpu"] = round(tflops / result["cpu_baseline"]["value"], 1)
     print(json.dumps(result))
 
 
