@@ -62,10 +62,11 @@ def test_full_size_batched_decode(batch):
     check_close(got, oracle_all(wl), "bf16", "batched decode")
 
 
-@pytest.mark.parametrize("group,batch", [(2, 16), (8, 16), (8, 64)])
+@pytest.mark.parametrize("group,batch", [(1, 16), (2, 16), (8, 16), (8, 64)])
 def test_full_size_group_sizes(group, batch):
-    """Full 4096-slot rings at the other group sizes of the matrix-core kernel: 32 query heads over
-    32 / G KV heads.  (2, 16): 2 splits per ring; (8, 16): 8 splits; (8, 64): 2 splits."""
+    """Full 4096-slot rings at the other group sizes: 32 query heads over 32 / G KV heads.
+    (1, 16): the VALU kernel, 4 splits per ring; matrix-core kernel: (2, 16) 2 splits per ring,
+    (8, 16) 8 splits, (8, 64) 2 splits."""
     hkv = 32 // group
     pos = np.random.default_rng(1100 + group + batch).integers(4096, 32768, size=batch)
     wl = make_workload(f"groups-{group}-{batch}", 1200 + group + batch, [(int(p), 1) for p in pos], window=4096,
