@@ -193,6 +193,25 @@ def test_workspace_plan():
     assert swa.swa_decode_workspace_size(cache(window=0), 2, 32) == 0       # invalid -> 0
 
 
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("window", [1, 255, 256, 1000, 4096, 4097, 32768])
+def test_workspace_plan_rule(group, window):
+    """The decode plan: the matrix-core kernel (G >= 2) aims at 512 workgroups,
+    the VALU kernel (G = 1) at 2048; a split of a full window keeps >= 256 slots
+    (in multiples of 32); the workspace holds B x Hq x splits x (D + 2) floats
+    when the window is split, nothing otherwise."""
+    hkv = 32 // group
+    c = cache(window=window, n_cache=4096, n_kv_heads=hkv)
+    for b in (1, 3, 8, 16, 64, 256, 4096):
+        target = 512 if group >= 2 else 2048
+        splits = min(max(1, window // 256), max(1, -(-target // (b * hkv))))
+        length = -(-window // splits)
+        length = -(-length // 32) * 32
+        splits = -(-window // length)
+        want = b * 32 * splits * (128 + 2) * 4 if splits > 1 else 0
+        assert swa.swa_decode_workspace_size(c, b, 32) == want, (b, splits, length)
+
+
 def test_empty_batch_is_a_no_op():
     c = cache()
     assert write(c, HostBatch([], [])) == swa.SWA_OK
