@@ -154,9 +154,18 @@ int swa_prefill_chunk(const swa_cache *cache, const swa_batch *batch,
                       float sm_scale, void *out, void *stream);
 
 /*
- * Bytes of device workspace swa_decode needs for this cache shape, batch size
- * and head count (0 when the plan needs none).  Returns 0 for invalid input.
+ * Bytes of device workspace swa_decode and swa_decode_step need for this cache
+ * shape, batch size and head count (0 when the plan needs none).  Returns 0 for
+ * invalid input.  The plan may split each sequence's window into S parts that
+ * separate workgroups attend to; the workspace then holds one partial result
+ * of head_dim + 2 floats per (sequence, query head, part), i.e.
+ * num_seqs * n_q_heads * S * (head_dim + 2) * 4 bytes, and a merge launch
+ * combines them.  Guarantees: S depends only on the arguments of this call;
+ * 1 <= S <= max(1, window / 128); S = 1 (no workspace) when num_seqs *
+ * n_kv_heads >= 2048 or for SWA_DTYPE_F32; and the total never exceeds
+ * SWA_DECODE_WORKSPACE_MAX_BYTES.
  */
+#define SWA_DECODE_WORKSPACE_MAX_BYTES ((size_t)8 << 20)
 size_t swa_decode_workspace_size(const swa_cache *cache, int32_t num_seqs, int32_t n_q_heads);
 
 /*

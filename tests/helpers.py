@@ -6,7 +6,7 @@ import numpy as np
 
 import oracle
 import sliding_window_gqa_swa_amd as swa
-from sliding_window_gqa_swa_amd.workloads import Workload, to_f32
+from sliding_window_gqa_swa_amd.workloads import Workload, bf16_bits_from_f32, to_f32
 
 BF16_NAN = 0x7FC0
 TOL = {"bf16": 2e-2, "f32": 1e-4}   # max-abs error bars for attention outputs
@@ -113,3 +113,21 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
         rel = float(np.sqrt((err ** 2).sum() / max((ref ** 2).sum(), 1e-300)))
         assert rel <= REL_RMS_BF16, f"{what}: rel-RMS {rel:.3e} > {REL_RMS_BF16}"
     return mx
+
+
+def one_hot_v(n_pos, hkv, d, dtype, base=0):
+    """Value row of position j: one-hot(j mod 64) in dims 0..63, one-hot(j // 64 mod 64) in 64..127."""
+    v = np.zeros((n_pos, hkv, d), np.float32)
+    for r in range(n_pos):
+        j = base + r
+        v[r, :, j % 64] = 1.0
+        v[r, :, 64 + (j // 64) % 64] = 1.0
+    return bf16_bits_from_f32(v) if dtype == "bf16" else v
+
+
+def expected_hist(i, window):
+    """Histogram of the one-hot codes of the positions in J(i) = [max(0, i-W+1), i], and |J(i)|."""
+    band = np.arange(max(0, i - window + 1), i + 1)
+    lo = np.bincount(band % 64, minlength=64)
+    hi = np.bincount((band // 64) % 64, minlength=64)
+    return np.concatenate([lo, hi]).astype(np.float64), len(band)

@@ -194,22 +194,27 @@ def test_workspace_plan():
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("window", [1, 255, 256, 1000, 4096, 4097, 32768])
-def test_workspace_plan_rule(group, window):
-    """The decode plan: the matrix-core kernel (G >= 2) aims at 512 workgroups,
-    the VALU kernel (G = 1) at 2048; a split of a full window keeps >= 256 slots
-    (in multiples of 32); the workspace holds B x Hq x splits x (D + 2) floats
-    when the window is split, nothing otherwise."""
+@pytest.mark.parametrize("window", [1, 127, 128, 255, 256, 1000, 4096, 4097, 32768, 2**20])
+@pytest.mark.parametrize("head_dim", [128])
+def test_workspace_size_guarantees(group, window, head_dim):
+    """The guarantees stated with swa_decode_workspace_size: the size is a whole
+    number S of per-part partial results (head_dim + 2 floats per sequence and
+    query head), 1 <= S <= max(1, W / 128), no workspace once the batch alone
+    gives 2048 (sequence, KV head) pairs, and never more than the stated maximum."""
     hkv = 32 // group
-    c = cache(window=window, n_cache=4096, n_kv_heads=hkv)
-    for b in (1, 3, 8, 16, 64, 256, 4096):
-        target = 512 if group >= 2 else 2048
-        splits = min(max(1, window // 256), max(1, -(-target // (b * hkv))))
-        length = -(-window // splits)
-        length = -(-length // 32) * 32
-        splits = -(-window // length)
-        want = b * 32 * splits * (128 + 2) * 4 if splits > 1 else 0
-        assert swa.swa_decode_workspace_size(c, b, 32) == want, (b, splits, length)
+    c = cache(window=window, n_cache=65535, n_kv_heads=hkv, head_dim=head_dim)
+    max_bytes = int(re.search(r"#define SWA_DECODE_WORKSPACE_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                              open(HEADER).read()).group(1)) << 20
+    for b in list(range(1, 70)) + [127, 128, 129, 255, 256, 511, 512, 513, 4095, 4096, 65535]:
+        sz = swa.swa_decode_workspace_size(c, b, 32)
+        per_part = b * 32 * (head_dim + 2) * 4
+        assert sz % per_part == 0, (b, sz)
+        parts = max(1, sz // per_part)
+        assert 1 <= parts <= max(1, window // 128), (b, parts)
+        if b * hkv >= 2048:
+            assert sz == 0, b
+        assert sz <= max_bytes, (b, sz)
+    assert swa.swa_decode_workspace_size(cache(window=window, dtype=swa.SWA_DTYPE_F32, n_kv_heads=hkv), 1, 32) == 0
 
 
 def test_empty_batch_is_a_no_op():

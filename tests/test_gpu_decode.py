@@ -10,7 +10,8 @@ import pytest
 
 import sliding_window_gqa_swa_amd as swa
 from sliding_window_gqa_swa_amd.workloads import batched_decode, make_workload
-from helpers import check_close, host_f32, host_raw, oracle_all, poisoned_cache, run_decode, write_history
+from helpers import (check_close, dev, expected_hist, host_f32, host_raw, one_hot_v, oracle_all, poisoned_cache,
+                     run_decode, torch, write_history)
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +105,82 @@ def test_deterministic_bitwise():
 def test_position_next_to_int32_max(dtype):
     d = 128 if dtype == "bf16" else 16
     decode_case(61, [2**31 - 2, 2**31 - 5000], 4096 if dtype == "bf16" else 64, 8, 2, d, dtype)
+
+
+MASK_POSITIONS = [0, 1, 127, 128, 511, 512, 513, 2047, 4094, 4095, 4096, 9000, 255, 256, 1023, 1024]
+
+
+def mask_workload(positions, group, seed):
+    """Q = 0 and K = 0 give every valid slot the weight 1/|J(pos)|; V of position j is
+    one-hot(j mod 64) + one-hot(64 + (j // 64) mod 64), so O * |J(pos)| is the exact
+    histogram of the positions the query attended to."""
+    hkv = 32 // group
+    wl = make_workload("dmask", seed, [(p, 1) for p in positions], window=4096, n_q_heads=32, n_kv_heads=hkv,
+                       head_dim=128, dtype="bf16")
+    wl.q[:] = 0
+    wl.k_new[:] = 0
+    wl.v_new = np.concatenate([one_hot_v(1, hkv, 128, "bf16", base=p) for p in positions])
+    for b, s in enumerate(wl.seqs):
+        wl.hist_k[b][:] = 0
+        wl.hist_v[b] = one_hot_v(s.start_pos - s.hist_lo, hkv, 128, "bf16", base=s.hist_lo)
+    return wl
+
+
+def assert_mask_histograms(got, wl, group, what):
+    for b, s in enumerate(wl.seqs):
+        exp, cnt = expected_hist(s.start_pos, 4096)
+        for h in sorted({0, group - 1, group % 32, 31}):
+            hist = np.rint(got[b, h].astype(np.float64) * cnt)
+            assert np.array_equal(hist, exp), (what, s.start_pos, h)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("batch", [8, 16])
+@pytest.mark.parametrize("fused", [False, True])
+def test_mask_extraction_at_split_boundaries(group, batch, fused):
+    """W = 4096 with 8 or 16 sequences: the plan splits every window (4 to 16 splits),
+    and each sequence spreads its valid slots over the splits, so positions next to
+    127/128, 511/512, 2047, 4095/4096 put the window edge and the new token's slot
+    on split boundaries.  One slot dropped or counted twice changes the histogram."""
+    hkv = 32 // group
+    assert swa.swa_decode_workspace_size(poisoned_cache(1, hkv, 4096, 128, "bf16"), batch, 32) > 0
+    for part in range(0, len(MASK_POSITIONS), batch):
+        positions = MASK_POSITIONS[part:part + batch]
+        wl = mask_workload(positions, group, seed=900 + part)
+        cache = poisoned_cache(batch, hkv, 4096, 128, "bf16")
+        write_history(cache, wl)
+        t = torch()
+        bt = swa.Batch([1] * batch, positions, list(range(batch)))
+        q, kn, vn = dev(wl.q, "bf16"), dev(wl.k_new, "bf16"), dev(wl.v_new, "bf16")
+        out = t.full((batch, 32, 128), float("nan"), dtype=t.bfloat16, device="cuda")
+        nb = swa.swa_decode_workspace_size(cache, batch, 32)
+        ws = t.empty(nb, dtype=t.uint8, device="cuda")
+        if fused:
+            swa.swa_decode_step(cache, bt, q, 32, kn, vn, wl.scale, out, ws, nb)
+        else:
+            swa.swa_cache_write(cache, bt, kn, vn)
+            swa.swa_decode(cache, bt, q, 32, wl.scale, out, ws, nb)
+        assert_mask_histograms(host_f32(out, "bf16"), wl, group, f"G={group} B={batch} fused={fused}")
+
+
+@pytest.mark.parametrize("group", [1, 4, 8])
+def test_workspace_of_the_stated_size_is_enough(group):
+    """swa_decode uses no byte past swa_decode_workspace_size(): the bytes after it
+    keep a guard pattern, and the result matches the oracle."""
+    hkv = 32 // group
+    positions = [4100, 77, 20000]
+    wl = make_workload("guard", 31 + group, [(p, 1) for p in positions], window=4096, n_q_heads=32,
+                       n_kv_heads=hkv, head_dim=128, dtype="bf16")
+    cache = poisoned_cache(3, hkv, 4096, 128, "bf16")
+    write_history(cache, wl)
+    t = torch()
+    nb = swa.swa_decode_workspace_size(cache, 3, 32)
+    assert nb > 0
+    buf = t.full((nb + 4096,), 0xA5, dtype=t.uint8, device="cuda")
+    bt = swa.Batch([1] * 3, positions)
+    swa.swa_cache_write(cache, bt, dev(wl.k_new, "bf16"), dev(wl.v_new, "bf16"))
+    out = t.full((3, 32, 128), float("nan"), dtype=t.bfloat16, device="cuda")
+    swa.swa_decode(cache, bt, dev(wl.q, "bf16"), 32, wl.scale, out, buf, nb)
+    t.cuda.synchronize()
+    assert bool((buf[nb:] == 0xA5).all())
+    check_close(host_f32(out, "bf16"), oracle_all(wl), "bf16", f"guarded workspace G={group}")

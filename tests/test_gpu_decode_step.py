@@ -51,7 +51,8 @@ def assert_same_bits(a, b, what):
 
 
 @pytest.mark.parametrize("dtype,window,group", [("bf16", 4096, 4), ("bf16", 100, 8), ("bf16", 1, 1),
-                                                ("bf16", 300, 2), ("f32", 64, 4), ("f32", 5, 1)])
+                                                ("bf16", 4096, 1), ("bf16", 1000, 1), ("bf16", 300, 2),
+                                                ("f32", 64, 4), ("f32", 5, 1)])
 def test_fused_step_equals_write_then_decode(dtype, window, group):
     hkv = 2
     d = 128 if dtype == "bf16" else 16
@@ -65,6 +66,24 @@ def test_fused_step_equals_write_then_decode(dtype, window, group):
     assert_same_bits(c_sep.k, c_fus.k, "cache K")
     assert_same_bits(c_sep.v, c_fus.v, "cache V")
     check_close(host_f32(o_fus, dtype), oracle_all(wl), dtype, f"fused step W={window}")
+
+
+@pytest.mark.parametrize("group,batch", [(1, 16), (1, 64)])
+def test_fused_step_full_size_other_groups(group, batch):
+    """Full 4096-slot rings with 32 query heads over 32 / G KV heads.  G = 1 runs on
+    the VALU kernel: 16 sequences x 32 KV heads split every window in 4, so the new
+    token's slot lands in a split sp > 0 for most sequences; 64 sequences need no split."""
+    hkv = 32 // group
+    pos = np.random.default_rng(1300 + group + batch).integers(4096, 32768, size=batch)
+    wl = make_workload(f"step-g{group}", 1400 + group + batch, [(int(p), 1) for p in pos], window=4096,
+                       n_q_heads=32, n_kv_heads=hkv, head_dim=128, dtype="bf16")
+    cache = poisoned_cache(batch, hkv, 4096, 128, "bf16")
+    write_history(cache, wl)
+    (c_sep, o_sep), (c_fus, o_fus) = separate_and_fused(wl, cache)
+    assert_same_bits(o_sep, o_fus, "output")
+    assert_same_bits(c_sep.k, c_fus.k, "cache K")
+    assert_same_bits(c_sep.v, c_fus.v, "cache V")
+    check_close(host_f32(o_fus, "bf16"), oracle_all(wl), "bf16", f"fused step G={group} B={batch}")
 
 
 @pytest.mark.parametrize("batch", [64, 8])

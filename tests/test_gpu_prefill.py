@@ -14,8 +14,8 @@ import oracle
 import sliding_window_gqa_swa_amd as swa
 from oracle.brute import brute_masked_attention
 from sliding_window_gqa_swa_amd.workloads import make_workload, tiny_prefill, to_f32
-from helpers import (check_close, dev, empty, host_f32, host_raw, new_batch, oracle_all, poisoned_cache,
-                     run_prefill, torch, write_history)
+from helpers import (check_close, dev, empty, expected_hist, host_f32, host_raw, new_batch, one_hot_v, oracle_all,
+                     poisoned_cache, run_prefill, torch, write_history)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,35 +85,19 @@ def test_window_one_is_exact(dtype):
         assert np.array_equal(got[:, h, :], wl.v_new[:, h // 4, :])
 
 
-def one_hot_v(n_pos, hkv, d, dtype, base=0):
-    """Value row of position j: one-hot(j mod 64) in dims 0..63, one-hot(j // 64 mod 64) in 64..127."""
-    v = np.zeros((n_pos, hkv, d), np.float32)
-    for r in range(n_pos):
-        j = base + r
-        v[r, :, j % 64] = 1.0
-        v[r, :, 64 + (j // 64) % 64] = 1.0
-    from sliding_window_gqa_swa_amd.workloads import bf16_bits_from_f32
-    return bf16_bits_from_f32(v) if dtype == "bf16" else v
-
-
-def expected_hist(i, window):
-    band = range(max(0, i - window + 1), i + 1)
-    lo, hi = np.zeros(64), np.zeros(64)
-    for j in band:
-        lo[j % 64] += 1
-        hi[(j // 64) % 64] += 1
-    return np.concatenate([lo, hi]), len(band)
-
-
-@pytest.mark.parametrize("window", [1, 2, 3, 4, 8, 17, 63, 64, 65, 127, 128, 129, 4096])
-def test_mask_extraction_bf16(window):
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("window", [1, 2, 3, 4, 8, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 4096])
+def test_mask_extraction_bf16(window, group):
     """Q = 0 makes every weight 1/|J(i)|; one-hot V turns O * |J(i)| into the exact
     histogram of the attended positions, so any off-by-one at the window edge or the
-    diagonal shows, also through the ring (history) and the chunk boundary."""
+    diagonal shows, also through the ring (history) and the chunk boundary.  Every
+    compiled group size: a workgroup spans 256 / G query positions, so the band
+    loop bounds differ per G."""
     hkv, d = 2, 128
-    for start, n_new in [(0, 300), (200, 190), (5000, 70)]:
+    hq = hkv * group
+    for start, n_new in [(0, 300), (200, 190), (5000, 70), (4000, 600)]:
         hist_lo = max(0, start - window + 1)
-        wl = make_workload("mask", 1, [(start, n_new)], window=window, n_q_heads=8, n_kv_heads=hkv, head_dim=d,
+        wl = make_workload("mask", 1, [(start, n_new)], window=window, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
                            dtype="bf16")
         wl.q[:] = 0
         wl.k_new[:] = 0
@@ -125,7 +109,7 @@ def test_mask_extraction_bf16(window):
         got = host_f32(run_prefill(wl, cache), "bf16")
         for r in range(n_new):
             exp, cnt = expected_hist(start + r, window)
-            for h in (0, 7):
+            for h in sorted({0, group - 1, group, hq - 1}):
                 hist = np.rint(got[r, h].astype(np.float64) * cnt)
                 assert np.array_equal(hist, exp), (window, start, r, h)
 

@@ -191,6 +191,34 @@ def test_ring_matches_golden_tables(window, name):
             assert list(slots) == table[e], (chunks, e)
 
 
+def test_ring_batch_with_permuted_rows_matches_golden_table():
+    """One batched write of three ragged sequences into permuted cache rows
+    (cache_idx = 2, 0, 1), one of them longer than W: every slot of every row
+    and head against a table derived by hand from the slot rule (Mistral 7B
+    (Chinese translation), section 2, paragraph "Rolling Buffer Cache")."""
+    table = {row[0]: row[1:] for row in read_golden("ring_batch_w4.txt")}
+    window, hkv, d = 4, 2, 3
+    n_tok = 10
+    # packed input row t, head g carries (t, g, 7): a misplaced row, head or byte shows
+    rows = np.zeros((n_tok, hkv, d), np.int32)
+    for t in range(n_tok):
+        for g in range(hkv):
+            rows[t, g] = (t, g, 7)
+    ring = np.full((3, hkv, window, d), -1, np.int32)
+    oracle.ring_write(ring, rows, [0, 3, 9, 10], [2, 0, 9], [2, 0, 1])
+    for r in range(3):
+        for g in range(hkv):
+            for slot in range(window):
+                t = table[r][slot]
+                expect = [-1, -1, -1] if t < 0 else [t, g, 7]
+                assert list(ring[r, g, slot]) == expect, (r, g, slot)
+    # the same batch without cache_idx writes sequence b into row b
+    ring2 = np.full((3, hkv, window, d), -1, np.int32)
+    oracle.ring_write(ring2, rows, [0, 3, 9, 10], [2, 0, 9], None)
+    for b, r in enumerate([2, 0, 1]):
+        assert np.array_equal(ring2[b], ring[r])
+
+
 def test_chunked_prefill_through_ring_equals_unchunked():
     rng = np.random.default_rng(11)
     n, hkv, group, d = 50, 2, 2, 8
