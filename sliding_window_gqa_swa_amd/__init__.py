@@ -23,7 +23,7 @@ __all__ = [
     "SWA_ERR_WORKSPACE", "SWA_ERR_HIP", "SWA_ERR_INTERNAL", "SwaError", "SwaLibraryMissing",
     "SwaCacheC", "SwaBatchC", "Cache", "Batch", "lib", "lib_path",
     "swa_abi_version", "swa_status_string", "swa_cache_write", "swa_prefill_chunk",
-    "swa_decode_workspace_size", "swa_decode",
+    "swa_decode_workspace_size", "swa_decode", "swa_decode_step",
 ]
 
 SWA_DTYPE_BF16 = 0

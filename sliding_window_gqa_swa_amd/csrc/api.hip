@@ -25,7 +25,7 @@ static bool aligned16(const void *p) { return (((uintptr_t)p) & 15u) == 0; }
 
 // Shapes the kernels are compiled for.
 static bool head_dim_supported(int32_t dtype, int32_t d) {
-  if (dtype == SWA_DTYPE_BF16) return d == 128;
+  (void)dtype;  // both dtypes are compiled for the same head dims
   return d == 16 || d == 64 || d == 128;
 }
 
@@ -121,9 +121,9 @@ static swa_status check_heads(const swa_cache *c, int32_t n_q_heads) {
 
 static bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
-// bf16 decode with G >= 2 query heads per KV head runs on the matrix cores
-// (decode_mfma.hip); G = 1 on the VALU kernel (decode_bf16.hip).
-constexpr int kMfmaMinGroup = 2;
+// bf16 decode runs on the matrix cores (decode_mfma.hip), except G = 1 at
+// head_dim 128, which has its own VALU kernel (decode_bf16.hip).
+static bool decode_on_valu(int32_t group, int32_t head_dim) { return group == 1 && head_dim == 128; }
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, int32_t head_dim, int32_t window,
                        int32_t dtype) {
@@ -135,7 +135,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   // ring and need no merge launch.  A split keeps >= 256 slots either way, so
   // that each wave streams several 16 KiB steps.
   const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
-  const int64_t target_wg = n_q_heads / n_kv_heads >= kMfmaMinGroup ? 512 : 2048;
+  const int64_t target_wg = decode_on_valu(n_q_heads / n_kv_heads, head_dim) ? 2048 : 512;
   int64_t max_splits = std::max<int64_t>(1, window / 256);
   int64_t splits = std::min<int64_t>(max_splits, std::max<int64_t>(1, (target_wg + pairs - 1) / pairs));
   int64_t len = (window + splits - 1) / splits;
@@ -191,8 +191,8 @@ static int decode_impl(const swa_cache *cache, const swa_batch *batch, const voi
   hipError_t e;
   const int group = n_q_heads / cache->n_kv_heads;
   if (cache->dtype == SWA_DTYPE_BF16)
-    e = group >= kMfmaMinGroup ? launch_decode_mfma_bf16(p, group, stream)
-                                        : launch_decode_bf16(p, group, stream);
+    e = decode_on_valu(group, cache->head_dim) ? launch_decode_bf16(p, group, stream)
+                                               : launch_decode_mfma_bf16(p, group, stream);
   else
     e = launch_decode_f32(p, stream);
   return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;

@@ -12,10 +12,11 @@
 // positions max(0, pos-W+1) .. pos, so the query attends to every valid slot;
 // softmax attention is a sum over keys and needs no slot -> position map.
 //
-// The library launches this kernel for G = 1 only; G = 2, 4, 8 run on the
-// matrix cores (decode_mfma.hip), because the per-head VALU work here grows
-// with G.  The template still handles G <= 8, and the split merge (combine
-// kernel) below serves both kernels.
+// The library launches this kernel for G = 1 at head_dim 128 only; G = 2, 4,
+// 8 (and head_dim 16 / 64 at any G) run on the matrix cores (decode_mfma.hip),
+// because the per-head VALU work here grows with G.  The template still
+// handles G <= 8, and the split merge (combine kernel) below serves both
+// kernels at every head_dim.
 //
 // Design (HBM-bound: 4 FLOP per byte of K/V):
 //   * One workgroup = (sequence, KV head, split of the window): 4 waves.  All
@@ -233,12 +234,14 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
 // Merge the per-split partials of each (sequence, query head).  The partials
 // are read kBatch at a time (independent loads in flight together); the sums
 // still run in split order.  An empty split (max -inf) has weight 0.
+// One thread per output element: blockDim = head_dim.
 __global__ __launch_bounds__(kD) void decode_combine_bf16_kernel(DecodeParams p) {
   constexpr int kBatch = 8;
   const int bh = blockIdx.x, d = threadIdx.x;
+  const int D = p.cache.head_dim;
   const int S = p.splits;
   const float *ml = p.ws_ml + (size_t)bh * S * 2;
-  const float *acc = p.ws_acc + (size_t)bh * S * kD;
+  const float *acc = p.ws_acc + (size_t)bh * S * D;
   float mx = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += kBatch) {
     float mv[kBatch];
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kD) void decode_combine_bf16_kernel(DecodeParams p)
       const bool in = s0 + i < S;
       mv[i] = in ? ml[2 * (s0 + i)] : -INFINITY;
       lv[i] = in ? ml[2 * (s0 + i) + 1] : 0.f;
-      av[i] = in ? acc[(size_t)(s0 + i) * kD + d] : 0.f;
+      av[i] = in ? acc[(size_t)(s0 + i) * D + d] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kBatch; i++) {
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(kD) void decode_combine_bf16_kernel(DecodeParams p)
       os += av[i] * f;
     }
   }
-  ((uint16_t *)p.out)[(size_t)bh * kD + d] = (uint16_t)pack_bf16(os / ls, 0.f);
+  ((uint16_t *)p.out)[(size_t)bh * D + d] = (uint16_t)pack_bf16(os / ls, 0.f);
 }
 
 template <int G>
@@ -281,14 +284,14 @@ hipError_t launch_g(const DecodeParams &p, hipStream_t stream) {
 
 hipError_t launch_decode_combine_bf16(const DecodeParams &p, hipStream_t stream) {
   if (p.seq.num_seqs == 0 || p.splits == 1) return hipSuccess;
-  hipLaunchKernelGGL(decode_combine_bf16_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads), dim3(kD), 0, stream,
-                     p);
+  hipLaunchKernelGGL(decode_combine_bf16_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads),
+                     dim3((unsigned)p.cache.head_dim), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_bf16(const DecodeParams &p, int group, hipStream_t stream) {
   if (p.seq.num_seqs == 0) return hipSuccess;
-  if (group != 1) return hipErrorInvalidValue;
+  if (group != 1 || p.cache.head_dim != kD) return hipErrorInvalidValue;
   return launch_g<1>(p, stream);
 }
 

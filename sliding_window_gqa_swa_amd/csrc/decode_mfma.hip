@@ -1,5 +1,6 @@
 // Single-token sliding-window GQA decode on the matrix cores, bf16, gfx950
-// (G = 2, 4, 8 query heads per KV head).
+// (G = 2, 4, 8 query heads per KV head at head_dim 128; every G at head_dim
+// 16 and 64).
 //
 // Same operation as decode_bf16.hip (Mistral 7B (Chinese translation),
 // section 2, paragraphs "Rolling Buffer Cache" and "Pre-fill and Chunking";
@@ -35,12 +36,9 @@
 namespace swa {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;                  // keys per wave step
-constexpr int kRowB = kD * 2;              // 256-byte rows
-constexpr int kVBufB = kStep * kRowB;      // 8 KiB per wave and buffer
 constexpr float kRescaleSlack = 8.0f;      // log2 units, as in the prefill
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 constexpr int kNonTemporal = 2;  // cache-policy bit "nt" of a global_load_lds (K rows use nontemporal loads too)
@@ -63,11 +61,36 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int G>
+// Row geometry for head_dim D (128, 64 or 16): a row is 2D bytes in kC
+// chunks of 16 bytes; one global_load_lds moves 1 KiB = kRpl rows; the V rows
+// are stored in 32-byte segments XOR-swizzled by vseg(row) (the prefill's V
+// layout), so a transposed read of 8 consecutive rows hits 8 different bank
+// groups.
+template <int D>
+struct RowGeo {
+  static constexpr int kRowB = 2 * D;
+  static constexpr int kVBufB = kStep * kRowB;         // one wave step of V rows
+  static constexpr int kC = D / 8;
+  static constexpr int kRpl = 64 / kC;
+  static constexpr int kVLoads = kStep / kRpl;         // 1 KiB loads per V step (8, 4, 1)
+  static constexpr int kKS = D >= 32 ? D / 32 : 1;     // 32-deep steps of QK (D = 16: zero-padded)
+  static constexpr int kDB = D / 16;
+  static __device__ __forceinline__ int vseg(int row) {
+    if constexpr (D == 128) return (row & 3) + 4 * ((row >> 2) & 1);
+    else if constexpr (D == 64) return (row >> 1) & 3;
+    else return 0;
+  }
+};
+
+template <int G, int D>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  using Rg = RowGeo<D>;
+  constexpr int kD = D, kRowB = Rg::kRowB, kVBufB = Rg::kVBufB, kC = Rg::kC, kRpl = Rg::kRpl;
+  constexpr int kKS = Rg::kKS, kDB = Rg::kDB;
   // two V buffers per wave, as two objects; after the loop vbuf_a holds the merge
   __shared__ __attribute__((aligned(16))) unsigned char vbuf_a[kWaves][kVBufB];
   __shared__ __attribute__((aligned(16))) unsigned char vbuf_b[kWaves][kVBufB];
+  static_assert(kWaves * G * (kD + 2) * 4 <= kWaves * kVBufB, "the wave merge fits in vbuf_a");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -99,54 +122,54 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int new_slot = fused ? pos % W : -1;
   const uint16_t *knew = fused ? (const uint16_t *)p.k_new + ((size_t)b * hkv + g) * kD : nullptr;
   const uint16_t *vnew = fused ? (const uint16_t *)p.v_new + ((size_t)b * hkv + g) * kD : nullptr;
-  if (new_slot >= r_begin && new_slot < r_end && wave == 0 && lane < 32) {
-    const int ch = lane & 15;
-    const uint16_t *src = lane < 16 ? knew : vnew;
-    uint16_t *dst = (uint16_t *)(lane < 16 ? p.cache_k_out : p.cache_v_out) + ring0 + (size_t)new_slot * kD;
+  if (new_slot >= r_begin && new_slot < r_end && wave == 0 && lane < 2 * kC) {
+    // kC lanes copy the K row, kC lanes the V row, 16 bytes each
+    const int ch = lane % kC;
+    const uint16_t *src = lane < kC ? knew : vnew;
+    uint16_t *dst = (uint16_t *)(lane < kC ? p.cache_k_out : p.cache_v_out) + ring0 + (size_t)new_slot * kD;
     *(u32x4 *)(dst + 8 * ch) = *(const u32x4 *)(src + 8 * ch);
   }
 
-  bf16x8 qf[4];  // Q^T as the B operand, loaded after the first K/V loads are issued
+  bf16x8 qf[kKS];  // Q^T as the B operand, loaded after the first K/V loads are issued
 
   // LDS offsets of the transposed V reads (the prefill's mapping for one
-  // 32-key slice): rows 4 lg + (col / 4) and +16, 8 bytes at chunk-swizzled
-  // columns; v_off[h][dl] for d-block db = 4 h + dl
-  int v_off[2][4];
+  // 32-key slice): rows 4 lg + (col / 4) and +16, 8 bytes at segment-swizzled
+  // columns of d-block db
+  int v_off[kDB];
   {
     const int vr = 4 * lg + (col >> 2);
-    const int j = vr & 3, hv = (vr >> 2) & 1;
     const int vb = vr * kRowB + 8 * (lane & 3);
 #pragma unroll
-    for (int dl = 0; dl < 4; dl++) {
-      v_off[0][dl] = vb + 32 * (dl ^ j) + 128 * hv;
-      v_off[1][dl] = vb + 32 * (dl ^ j) + 128 * (hv ^ 1);
-    }
+    for (int db = 0; db < kDB; db++) v_off[db] = vb + 32 * (db ^ Rg::vseg(vr));
   }
-  // global_load_lds of a V step: load i (0..7) covers rows 4 i .. 4 i + 3; lane
-  // -> row 4 i + lg, LDS chunk col, holding logical chunk col ^ swizzle(row)
-  // with swizzle(row) = 2 (row % 4) + 8 ((row / 4) % 2) = 2 lg + 8 (i % 2)
-  const int vchunk_even = col ^ (2 * lg);
-  const int vchunk_odd = col ^ (2 * lg) ^ 8;
+  // global_load_lds of a V step: load i covers rows kRpl i .. kRpl (i + 1) - 1;
+  // lane -> row kRpl i + lane / kC, LDS chunk lane % kC, holding logical chunk
+  // (lane % kC) ^ 2 vseg(row).  vseg of those rows depends on i only through
+  // its parity (D = 128: rows 4 i + lane / 16), so two values per lane suffice.
+  const int vchunk_even = (lane % kC) ^ (2 * Rg::vseg(lane / kC));
+  const int vchunk_odd = (lane % kC) ^ (2 * Rg::vseg(kRpl + lane / kC));
 
-  f32x4 o[8];
+  f32x4 o[kDB];
 #pragma unroll
-  for (int db = 0; db < 8; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < kDB; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;  // running max of this lane's column, log2 units
   float l = 0.f;        // this lane's share of the column's sum
 
-  // issue the loads of the step at r0: K rows into kf, V rows into vb (LDS)
-  auto issue = [&](int r0, bf16x8 (&kf)[2][4], unsigned char *vb) __attribute__((always_inline)) {
+  // issue the loads of the step at r0: K rows into kf, V rows into vb (LDS).
+  // (D = 16: lanes 32-63 load the row's two chunks again; their Q is zero)
+  auto issue = [&](int r0, bf16x8 (&kf)[2][kKS], unsigned char *vb) __attribute__((always_inline)) {
     const int last = r_end - 1;
 #pragma unroll
     for (int kbi = 0; kbi < 2; kbi++) {
       const int r = min(r0 + 16 * kbi + col, last);
       const uint16_t *kr = r == new_slot ? knew : kring + (size_t)r * kD;
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) kf[kbi][ks] = __builtin_nontemporal_load((const bf16x8 *)(kr + 32 * ks + 8 * lg));
+      for (int ks = 0; ks < kKS; ks++)
+        kf[kbi][ks] = __builtin_nontemporal_load((const bf16x8 *)(kr + 32 * ks + 8 * (lg & (kC - 1))));
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int r = min(r0 + 4 * i + lg, last);
+    for (int i = 0; i < Rg::kVLoads; i++) {
+      const int r = min(r0 + kRpl * i + lane / kC, last);
       const uint16_t *vr = r == new_slot ? vnew : vring + (size_t)r * kD;
       const int ch = (i & 1) ? vchunk_odd : vchunk_even;
       __builtin_amdgcn_global_load_lds(vr + 8 * ch, (lds_void *)(vb + i * 1024), 16, 0, kNonTemporal);
@@ -154,12 +177,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   };
 
   // S^T of a step: keys 16 kbi + 4 lg + i of the step in sa[kbi][i], column = head
-  auto scores = [&](const bf16x8 (&kf)[2][4], f32x4 (&sa)[2]) __attribute__((always_inline)) {
+  auto scores = [&](const bf16x8 (&kf)[2][kKS], f32x4 (&sa)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kbi = 0; kbi < 2; kbi++) {
       sa[kbi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) sa[kbi] = mfma16(kf[kbi][ks], qf[ks], sa[kbi]);
+      for (int ks = 0; ks < kKS; ks++) sa[kbi] = mfma16(kf[kbi][ks], qf[ks], sa[kbi]);
     }
   };
 
@@ -183,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       m = mn;
       l *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; db++) o[db] *= alpha;
+      for (int db = 0; db < kDB; db++) o[db] *= alpha;
     }
 #pragma unroll
     for (int kbi = 0; kbi < 2; kbi++)
@@ -198,8 +221,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     for (int e = 0; e < 4; e++) l = fdot2_bf16(w[e], kBf16OnePair, l);  // sum of what enters P V
     const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-    for (int db = 0; db < 8; db++) {
-      const unsigned char *va = vb + v_off[db >> 2][db & 3];
+    for (int db = 0; db < kDB; db++) {
+      const unsigned char *va = vb + v_off[db];
       const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
       const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowB));
       u32x4 vv;
@@ -218,15 +241,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int stride = kStep * kWaves;
   int r0 = r_begin + kStep * wave;
   const int n = r0 < r_end ? (r_end - r0 + stride - 1) / stride : 0;
-  bf16x8 ka[2][4], kb[2][4];
+  bf16x8 ka[2][kKS], kb[2][kKS];
   unsigned char *va = vbuf_a[wave], *vbb = vbuf_b[wave];
   if (n > 0) issue(r0, ka, va);
-  // Q^T: lane -> head `col` (zero when col >= G), d-group lg
+  // Q^T: lane -> head `col` (zero when col >= G), d-group lg (zero for lg >= 2 when D = 16)
   {
-    const bool ok = col < G;
-    const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * hq + g * G + (ok ? col : 0)) * kD + 8 * lg;
+    const bool ok = col < G && (kD >= 32 || lg < 2);
+    const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * hq + g * G + (ok ? col : 0)) * kD + 8 * (lg & (kC - 1));
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
+    for (int ks = 0; ks < kKS; ks++) {
       u32x4 v = {0, 0, 0, 0};
       if (ok) v = *(const u32x4 *)(qrow + 32 * ks);
       qf[ks] = __builtin_bit_cast(bf16x8, v);
@@ -262,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   float *sm_ml = sm_acc + kWaves * G * kD;          // [kWaves][G][2]
   if (col < G) {
 #pragma unroll
-    for (int db = 0; db < 8; db++)
+    for (int db = 0; db < kDB; db++)
 #pragma unroll
       for (int i = 0; i < 4; i++) sm_acc[(wave * G + col) * kD + 16 * db + 4 * lg + i] = o[db][i];
     if (lg == 0) {
@@ -301,23 +324,36 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <int G>
-hipError_t launch_g(const DecodeParams &p, hipStream_t stream) {
+template <int G, int D>
+hipError_t launch_gd(const DecodeParams &p, hipStream_t stream) {
   const unsigned n_wg = (unsigned)p.seq.num_seqs * p.cache.n_kv_heads * p.splits;
-  hipLaunchKernelGGL(decode_mfma_kernel<G>, dim3(n_wg), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, D>), dim3(n_wg), dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine_bf16(p, stream);
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams &p, int group, hipStream_t stream) {
+  switch (group) {
+    case 1:
+      if constexpr (D != 128) return launch_gd<1, D>(p, stream);  // D = 128, G = 1: the VALU kernel
+      return hipErrorInvalidValue;
+    case 2: return launch_gd<2, D>(p, stream);
+    case 4: return launch_gd<4, D>(p, stream);
+    case 8: return launch_gd<8, D>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma_bf16(const DecodeParams &p, int group, hipStream_t stream) {
   if (p.seq.num_seqs == 0) return hipSuccess;
-  switch (group) {
-    case 2: return launch_g<2>(p, stream);
-    case 4: return launch_g<4>(p, stream);
-    case 8: return launch_g<8>(p, stream);
+  switch (p.cache.head_dim) {
+    case 128: return launch_d<128>(p, group, stream);
+    case 64: return launch_d<64>(p, group, stream);
+    case 16: return launch_d<16>(p, group, stream);
     default: return hipErrorInvalidValue;
   }
 }

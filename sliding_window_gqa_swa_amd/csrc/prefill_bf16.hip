@@ -25,12 +25,14 @@
 //     issues MFMAs while the other runs the softmax.
 //   * Tiles go straight from global memory into LDS (global_load_lds, 16 bytes
 //     per lane): group A streams the K tiles (3 LDS slots), group B the V
-//     tiles (2 slots); no staging registers.  LDS rows are 256 B with XOR
-//     swizzles of the 16-byte chunks: K chunk ^ (row % 16) (the 16-byte K
-//     reads of 16 rows hit 16 different chunks), V chunk ^ (2 (row % 4) +
-//     8 ((row / 4) % 2)): a transposed read of 32 lanes covers rows 8k..8k+7,
-//     32 B each, and these land in 8 different 32-byte segments, i.e. all 64
-//     banks once.
+//     tiles (2 slots); no staging registers.  LDS rows are 2 head_dim bytes
+//     (256 B at head_dim 128) with XOR swizzles of the 16-byte chunks: at
+//     head_dim 128, K chunk ^ (row % 16) (the 16-byte K reads of 16 rows hit
+//     16 different chunks), V chunk ^ (2 (row % 4) + 8 ((row / 4) % 2)): a
+//     transposed read of 32 lanes covers rows 8k..8k+7, 32 B each, and these
+//     land in 8 different 32-byte segments, i.e. all 64 banks once (Geo<D>
+//     holds the same rules for head_dim 64 and 16).
+//   * head_dim 16 runs the 32-deep QK step with zero-padded Q (lanes 32-63).
 //   * Only tiles intersecting the workgroup's band [q0-W+1, q_last] are
 //     visited; only tiles crossing a row's window edge or the diagonal run the
 //     mask code.  Keys outside the band are never read from outside it: their
@@ -56,15 +58,38 @@
 namespace swa {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kBN = 64;                       // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowB = kD * 2;                 // 256-byte LDS rows
-constexpr int kTileB = kBN * kRowB;           // 16 KiB
-constexpr int kLdsBytes = 5 * kTileB;         // 3 K slots + 2 V slots
 constexpr float kRescaleSlack = 8.0f;         // log2 units: weights stay <= 256
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
+
+// Tile geometry for head_dim D (128, 64 or 16).  An LDS row holds one key (or
+// value) row of 2D bytes in 16-byte chunks; a tile is kBN rows.  One
+// global_load_lds instruction moves 1 KiB: kRpl rows of kC chunks.
+template <int D>
+struct Geo {
+  static constexpr int kRowB = 2 * D;                  // bytes per LDS row
+  static constexpr int kTileB = kBN * kRowB;           // 16 / 8 / 2 KiB
+  static constexpr int kLdsBytes = 5 * kTileB;         // 3 K slots + 2 V slots
+  static constexpr int kC = D / 8;                     // 16-byte chunks per row
+  static constexpr int kRpl = 64 / kC;                 // rows per 1 KiB wave-load
+  static constexpr int kNL = kBN / kRpl;               // wave-loads per tile
+  static constexpr int kLoads = (kNL + 3) / 4;         // wave-loads per wave of a group
+  static constexpr int kKS = D >= 32 ? D / 32 : 1;     // 32-deep steps of QK (D = 16: one, zero-padded)
+  static constexpr int kDB = D / 16;                   // 16-column blocks of O
+  // K rows: physical chunk = logical chunk ^ kswz(row).  The 16-byte operand
+  // reads of 16 consecutive rows then cover all 64 banks once.
+  static __device__ __forceinline__ int kswz(int row) { return (row / (16 / kC)) % kC; }
+  // V rows, in 32-byte segments: physical segment = logical ^ vseg(row).  A
+  // transposed read of 32 lanes covers 8 consecutive rows x 32 bytes of one
+  // logical segment, and these land in 8 different 32-byte bank groups.
+  static __device__ __forceinline__ int vseg(int row) {
+    if constexpr (D == 128) return (row & 3) + 4 * ((row >> 2) & 1);
+    else if constexpr (D == 64) return (row >> 1) & 3;
+    else return 0;
+  }
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -76,8 +101,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // LDS directly); expcnt and lgkmcnt are left unconstrained.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int G>
+template <int G, int D>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p) {
+  using Gm = Geo<D>;
+  constexpr int kRowB = Gm::kRowB, kTileB = Gm::kTileB, kC = Gm::kC, kRpl = Gm::kRpl;
+  constexpr int kKS = Gm::kKS, kDB = Gm::kDB;
   constexpr int kWph = kWaves / G;  // waves per query head
   constexpr int kBQ = 32 * kWph;    // query positions per workgroup
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -122,15 +150,16 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const float c = p.scale_log2;
 
   // ---- Q^T as MFMA B operand: lane -> query (lane & 15) of block qb, d-group (lane >> 4)
+  // (D = 16: the 32-deep MFMA step is zero-padded; lanes 32-63 hold zeros)
   const uint16_t *Q = (const uint16_t *)p.q;
-  bf16x8 qf[4][2];
+  bf16x8 qf[kKS][2];
 #pragma unroll
   for (int qb = 0; qb < 2; qb++) {
     const int qrel = qoff + 16 * qb + (lane & 15);
-    const bool ok = qrel < n_rows;
-    const uint16_t *qrow = Q + ((size_t)(tok0 + (q0 - s) + qrel) * hq + h) * kD + 8 * (lane >> 4);
+    const bool ok = qrel < n_rows && (D >= 32 || lane < 32);
+    const uint16_t *qrow = Q + ((size_t)(tok0 + (q0 - s) + qrel) * hq + h) * D + 8 * ((lane >> 4) & (kC - 1));
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
+    for (int ks = 0; ks < kKS; ks++) {
       u32x4 v = {0, 0, 0, 0};
       if (ok) v = *(const u32x4 *)(qrow + 32 * ks);
       qf[ks][qb] = __builtin_bit_cast(bf16x8, v);
@@ -138,14 +167,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   }
 
   // ---- Tile streaming.  Group A (waves 0-3) loads K tiles, group B (waves
-  // 4-7) V tiles.  A tile is 16 loads of 1 KiB (4 rows each); wave wg of its
-  // group issues loads wg, wg+4, wg+8, wg+12, i.e. rows 4*wg + 16*m + (lane/16),
-  // and its lane writes LDS chunk (lane % 16) of that row, which holds the
-  // logical chunk (lane % 16) ^ swizzle(row) -- a per-lane constant.
+  // 4-7) V tiles.  A tile is kNL loads of 1 KiB (kRpl rows each); wave wg of
+  // its group issues loads wg, wg+4, ..., i.e. rows kRpl*wg + 4*kRpl*m +
+  // (lane/kC), and its lane writes LDS chunk (lane % kC) of that row, which
+  // holds the logical chunk (lane % kC) ^ swizzle(row) -- a per-lane constant
+  // (the swizzles repeat every 4*kRpl rows).
   const int grp = wave >> 2, wg = wave & 3;
-  const int row_l = 4 * wg + (lane >> 4);            // row of load m is row_l + 16 m
-  const int pchunk = lane & 15;
-  const int lchunk = grp == 0 ? (pchunk ^ (row_l & 15)) : (pchunk ^ (2 * (row_l & 3)) ^ (8 * ((row_l >> 2) & 1)));
+  const int row_l = kRpl * wg + lane / kC;           // row of load m is row_l + 4 kRpl m
+  const int pchunk = lane % kC;
+  const int lchunk = grp == 0 ? (pchunk ^ Gm::kswz(row_l)) : (pchunk ^ (2 * Gm::vseg(row_l)));
   const char *src_ring = (const char *)(grp == 0 ? p.cache.k : p.cache.v);
   const char *src_new = (const char *)(grp == 0 ? p.k_new : p.v_new);
   const int64_t ring_row0 = ((int64_t)crow * hkv + g) * (int64_t)W;     // ring rows of (crow, g)
@@ -154,26 +184,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const uint32_t lane_off_new = (uint32_t)(row_l * hkv * kRowB + lchunk * 16);
   const uint32_t lane_off_ring = (uint32_t)(row_l * kRowB + lchunk * 16);
   auto load_tile = [&](unsigned char *dst, int ts) __attribute__((always_inline)) {
+    if (Gm::kNL < 4 && wg >= Gm::kNL) return;  // D = 16: a tile is two loads
     const bool all_valid = ts >= lo && ts + kBN - 1 <= hi;
     const int ts_mod = ts % W;
     // fast paths: a uniform base (scalar registers) plus this lane's 32-bit offset
     if (all_valid && ts >= s) {
       const char *base = src_new + ((new_tok0 + ts) * hkv + g) * (int64_t)kRowB;
 #pragma unroll
-      for (int m = 0; m < 4; m++)
-        __builtin_amdgcn_global_load_lds(base + (int64_t)(16 * m) * new_stride + lane_off_new,
+      for (int m = 0; m < Gm::kLoads; m++)
+        __builtin_amdgcn_global_load_lds(base + (int64_t)(4 * kRpl * m) * new_stride + lane_off_new,
                                          (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
     } else if (all_valid && ts + kBN - 1 < s && ts_mod + kBN <= W) {
       const char *base = src_ring + (ring_row0 + ts_mod) * kRowB;
 #pragma unroll
-      for (int m = 0; m < 4; m++)
-        __builtin_amdgcn_global_load_lds(base + 16 * m * kRowB + lane_off_ring,
+      for (int m = 0; m < Gm::kLoads; m++)
+        __builtin_amdgcn_global_load_lds(base + 4 * kRpl * m * kRowB + lane_off_ring,
                                          (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
     } else {
       // edge tile: rows outside [lo, hi] read the nearest key of the band
 #pragma unroll
-      for (int m = 0; m < 4; m++) {
-        const int j = min(max(ts + row_l + 16 * m, lo), hi);
+      for (int m = 0; m < Gm::kLoads; m++) {
+        const int j = min(max(ts + row_l + 4 * kRpl * m, lo), hi);
         const char *src = j < s ? src_ring + (ring_row0 + j % W) * kRowB
                                 : src_new + ((new_tok0 + j) * hkv + g) * (int64_t)kRowB;
         __builtin_amdgcn_global_load_lds(src + lchunk * 16, (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
@@ -185,27 +216,24 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 
   // LDS offsets of this lane's MFMA operand reads.
   //   K (A operand of S^T): row 16*kbi + lane%16, logical chunk 4*ks + lane/16
-  //     -> k_off[ks] + 4096*kbi
+  //     (D = 16: chunk (lane/16) % 2; lanes 32-63 meet zero Q) -> k_off[ks] + 16*kRowB*kbi
   //   V (transposed reads): rows 32*kk + 16*half + 4*(lane/16) + (lane%16)/4,
-  //     columns 16*db + 4*(lane%4) .. +4 -> v_off[db/4][db%4] + rows*256
-  int k_off[4], v_off[2][4];
+  //     columns 16*db + 4*(lane%4) .. +4 -> v_off[db] + rows*kRowB
+  // (the swizzles of rows r and r + 16 agree, so the offsets are per lane)
+  int k_off[kKS], v_off[kDB];
   {
     const int r = lane & 15;
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) k_off[ks] = r * kRowB + (((4 * ks + (lane >> 4)) ^ r) << 4);
+    for (int ks = 0; ks < kKS; ks++) k_off[ks] = r * kRowB + ((((4 * ks + (lane >> 4)) & (kC - 1)) ^ Gm::kswz(r)) << 4);
     const int vr = 4 * (lane >> 4) + ((lane & 15) >> 2);
-    const int j = vr & 3, hv = (vr >> 2) & 1;
     const int vb = vr * kRowB + 8 * (lane & 3);
 #pragma unroll
-    for (int dl = 0; dl < 4; dl++) {
-      v_off[0][dl] = vb + 32 * (dl ^ j) + 128 * hv;
-      v_off[1][dl] = vb + 32 * (dl ^ j) + 128 * (hv ^ 1);
-    }
+    for (int db = 0; db < kDB; db++) v_off[db] = vb + 32 * (db ^ Gm::vseg(vr));
   }
 
-  f32x4 o[8][2];
+  f32x4 o[kDB][2];
 #pragma unroll
-  for (int db = 0; db < 8; db++)
+  for (int db = 0; db < kDB; db++)
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Running max M of each query row's raw scores q.k, kept as the accumulator
@@ -230,10 +258,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
       for (int qb = 0; qb < 2; qb++) sa[kbi][qb] = negm[qb];
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
+    for (int ks = 0; ks < kKS; ks++) {
 #pragma unroll
       for (int kbi = 0; kbi < 4; kbi++) {
-        const bf16x8 kf = *(const bf16x8 *)(kb + k_off[ks] + 4096 * kbi);
+        const bf16x8 kf = *(const bf16x8 *)(kb + k_off[ks] + 16 * kRowB * kbi);
         sa[kbi][0] = mfma16(kf, qf[ks][0], sa[kbi][0]);
         sa[kbi][1] = mfma16(kf, qf[ks][1], sa[kbi][1]);
       }
@@ -243,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   // V^T fragment for O^T += V^T P^T: 16 d-columns (block db) x 32 keys (slice kk)
   // of the V tile at vbase, as two 4-key transposed reads per lane.
   auto vread = [&](const unsigned char *vbase, int kk, int db) __attribute__((always_inline)) {
-    const unsigned char *va = vbase + v_off[db >> 2][db & 3] + 32 * kk * kRowB;
+    const unsigned char *va = vbase + v_off[db] + 32 * kk * kRowB;
     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)va);
     const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(va + 16 * kRowB));
     u32x4 w;
@@ -268,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       const bf16x8 p0 = __builtin_bit_cast(bf16x8, pw[kk][0]);
       const bf16x8 p1 = __builtin_bit_cast(bf16x8, pw[kk][1]);
 #pragma unroll
-      for (int db = 0; db < 8; db++) {
+      for (int db = 0; db < kDB; db++) {
         const bf16x8 vf = vread(vbase, kk, db);
         o[db][0] = mfma16(vf, p0, o[db][0]);
         o[db][1] = mfma16(vf, p1, o[db][1]);
@@ -317,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         const float alpha = m_inf ? 0.f : __builtin_amdgcn_exp2f((mc - mn) * c);
         lsum[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 8; db++) o[db][qb] *= alpha;
+        for (int db = 0; db < kDB; db++) o[db][qb] *= alpha;
         const bool mn_inf = mn == -INFINITY;
         const float shift = mn_inf ? 0.f : mn - mc;  // 0 where M did not move
 #pragma unroll
@@ -367,7 +395,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   // still move the last QK MFMAs past the closing barrier; measured, that
   // beats keeping them inside.)
   auto schedule_matrix_half_step = [&]() __attribute__((always_inline)) {
-    constexpr int kReads = 48, kLead = 8, kPairs = (kReads - kLead) / 2;
+    constexpr int kReads = 4 * kDB + 4 * kKS;               // V reads, then K reads
+    constexpr int kMfma = 4 * kDB + 8 * kKS;                // P V, then Q K
+    constexpr int kLead = kReads < 8 ? kReads : 8, kPairs = (kReads - kLead) / 2;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // 0x100: LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // the row-sum MFMAs
 #pragma unroll
@@ -375,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // 0x008: MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 64 - 2 * kPairs, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - 2 * kPairs, 0);
   };
 
   auto step = [&](int t, bool masked, auto with_qk) __attribute__((always_inline)) {
@@ -425,9 +455,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const float inv = 1.0f / lt;
     const int qrel = qoff + 16 * qb + (lane & 15);
     if (qrel < n_rows) {
-      uint16_t *orow = O + ((size_t)(tok0 + (q0 - s) + qrel) * hq + h) * kD + 4 * (lane >> 4);
+      uint16_t *orow = O + ((size_t)(tok0 + (q0 - s) + qrel) * hq + h) * D + 4 * (lane >> 4);
 #pragma unroll
-      for (int db = 0; db < 8; db++) {
+      for (int db = 0; db < kDB; db++) {
         u32x2 w;
         w[0] = pack_bf16(o[db][qb][0] * inv, o[db][qb][1] * inv);
         w[1] = pack_bf16(o[db][qb][2] * inv, o[db][qb][3] * inv);
@@ -437,10 +467,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   }
 }
 
-template <int G>
-hipError_t launch_g(const PrefillParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_bf16_kernel<G>, dim3((unsigned)p.n_work), dim3(kThreads), kLdsBytes, stream, p);
+template <int G, int D>
+hipError_t launch_gd(const PrefillParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_bf16_kernel<G, D>), dim3((unsigned)p.n_work), dim3(kThreads), Geo<D>::kLdsBytes,
+                     stream, p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillParams &p, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_gd<1, D>(p, stream);
+    case 2: return launch_gd<2, D>(p, stream);
+    case 4: return launch_gd<4, D>(p, stream);
+    case 8: return launch_gd<8, D>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -449,11 +491,10 @@ int prefill_bf16_tile_rows(int group) { return 32 * (kWaves / group); }
 
 hipError_t launch_prefill_bf16(const PrefillParams &p, int group, hipStream_t stream) {
   if (p.n_work == 0) return hipSuccess;
-  switch (group) {
-    case 1: return launch_g<1>(p, stream);
-    case 2: return launch_g<2>(p, stream);
-    case 4: return launch_g<4>(p, stream);
-    case 8: return launch_g<8>(p, stream);
+  switch (p.cache.head_dim) {
+    case 128: return launch_d<128>(p, group, stream);
+    case 64: return launch_d<64>(p, group, stream);
+    case 16: return launch_d<16>(p, group, stream);
     default: return hipErrorInvalidValue;
   }
 }

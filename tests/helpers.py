@@ -116,18 +116,22 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
 
 
 def one_hot_v(n_pos, hkv, d, dtype, base=0):
-    """Value row of position j: one-hot(j mod 64) in dims 0..63, one-hot(j // 64 mod 64) in 64..127."""
+    """Value row of position j with h = d / 2: one-hot(j mod h) in dims 0..h-1 and
+    one-hot((j // h) mod h) in dims h..d-1 (h = 64 at head_dim 128)."""
+    h = d // 2
     v = np.zeros((n_pos, hkv, d), np.float32)
     for r in range(n_pos):
         j = base + r
-        v[r, :, j % 64] = 1.0
-        v[r, :, 64 + (j // 64) % 64] = 1.0
+        v[r, :, j % h] = 1.0
+        v[r, :, h + (j // h) % h] = 1.0
     return bf16_bits_from_f32(v) if dtype == "bf16" else v
 
 
-def expected_hist(i, window):
-    """Histogram of the one-hot codes of the positions in J(i) = [max(0, i-W+1), i], and |J(i)|."""
+def expected_hist(i, window, d=128):
+    """Histogram of the one-hot codes (see one_hot_v) of the positions in
+    J(i) = [max(0, i-W+1), i], and |J(i)|."""
+    h = d // 2
     band = np.arange(max(0, i - window + 1), i + 1)
-    lo = np.bincount(band % 64, minlength=64)
-    hi = np.bincount((band // 64) % 64, minlength=64)
+    lo = np.bincount(band % h, minlength=h)
+    hi = np.bincount((band // h) % h, minlength=h)
     return np.concatenate([lo, hi]).astype(np.float64), len(band)

@@ -98,19 +98,22 @@ def test_null_structs_are_rejected():
 @pytest.mark.parametrize("field,value,code", [
     ("window", 0, INVALID), ("n_cache", 0, INVALID), ("n_kv_heads", 0, INVALID), ("head_dim", 0, INVALID),
     ("dtype", 7, INVALID), ("reserved", 1, INVALID), ("k", FAKE + 8, INVALID), ("v", None, INVALID),
-    ("head_dim", 64, UNSUPPORTED), ("head_dim", 96, UNSUPPORTED), ("window", 2**30 + 1, UNSUPPORTED),
+    ("head_dim", 32, UNSUPPORTED), ("head_dim", 96, UNSUPPORTED), ("window", 2**30 + 1, UNSUPPORTED),
 ])
 def test_bad_cache_descriptor(field, value, code):
     c = cache(**{field: value})
     assert write(c, HostBatch([3], [0])) == code
 
 
-def test_fp32_head_dims():
+@pytest.mark.parametrize("dtype", [swa.SWA_DTYPE_BF16, swa.SWA_DTYPE_F32])
+def test_supported_head_dims(dtype):
     for d in (16, 64, 128):
-        c = cache(dtype=swa.SWA_DTYPE_F32, head_dim=d)
+        c = cache(dtype=dtype, head_dim=d)
         # rejected only for the bad sequence metadata that follows, not the shape
         assert write(c, HostBatch([3], [-1])) == INVALID
-    assert write(cache(dtype=swa.SWA_DTYPE_F32, head_dim=32), HostBatch([3], [0])) == UNSUPPORTED
+        assert prefill(c, HostBatch([3], [-1])) == INVALID
+    for d in (8, 32, 48, 256):
+        assert write(cache(dtype=dtype, head_dim=d), HostBatch([3], [0])) == UNSUPPORTED
 
 
 def test_bad_batch_metadata():

@@ -184,3 +184,50 @@ def test_workspace_of_the_stated_size_is_enough(group):
     t.cuda.synchronize()
     assert bool((buf[nb:] == 0xA5).all())
     check_close(host_f32(out, "bf16"), oracle_all(wl), "bf16", f"guarded workspace G={group}")
+
+
+@pytest.mark.parametrize("d", [16, 64])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_bf16_small_head_dims(d, group):
+    """head_dim 16 and 64 run on the matrix-core kernel at every G (G = 1 too)."""
+    hkv = 8 if group < 8 else 4
+    for window in (100, 4096):
+        positions = sorted({0, 1, window - 1, window, window + 1, 3 * window + 5, 20000})
+        decode_case(60 + d + group + window, positions, window, hkv * group, hkv, d, "bf16",
+                    rows=list(reversed(range(len(positions)))))
+
+
+@pytest.mark.parametrize("d,window", [(64, 4096), (16, 512)])
+@pytest.mark.parametrize("group", [1, 4])
+@pytest.mark.parametrize("fused", [False, True])
+def test_mask_extraction_small_head_dims(d, window, group, fused):
+    """Exact histograms at head_dim 64 and 16 with split plans (8 sequences)."""
+    hkv = 32 // group
+    positions = [0, 1, 127, 128, window - 2, window - 1, window, 9000]
+    wl = make_workload("dmask-d", 950 + d, [(p, 1) for p in positions], window=window, n_q_heads=32,
+                       n_kv_heads=hkv, head_dim=d, dtype="bf16")
+    wl.q[:] = 0
+    wl.k_new[:] = 0
+    wl.v_new = np.concatenate([one_hot_v(1, hkv, d, "bf16", base=p) for p in positions])
+    for b, s in enumerate(wl.seqs):
+        wl.hist_k[b][:] = 0
+        wl.hist_v[b] = one_hot_v(s.start_pos - s.hist_lo, hkv, d, "bf16", base=s.hist_lo)
+    cache = poisoned_cache(8, hkv, window, d, "bf16")
+    write_history(cache, wl)
+    t = torch()
+    bt = swa.Batch([1] * 8, positions, list(range(8)))
+    q, kn, vn = dev(wl.q, "bf16"), dev(wl.k_new, "bf16"), dev(wl.v_new, "bf16")
+    out = t.full((8, 32, d), float("nan"), dtype=t.bfloat16, device="cuda")
+    nb = swa.swa_decode_workspace_size(cache, 8, 32)
+    assert nb > 0
+    ws = t.empty(nb, dtype=t.uint8, device="cuda")
+    if fused:
+        swa.swa_decode_step(cache, bt, q, 32, kn, vn, wl.scale, out, ws, nb)
+    else:
+        swa.swa_cache_write(cache, bt, kn, vn)
+        swa.swa_decode(cache, bt, q, 32, wl.scale, out, ws, nb)
+    got = host_f32(out, "bf16")
+    for b, p in enumerate(positions):
+        exp, cnt = expected_hist(p, window, d)
+        for h in sorted({0, group - 1, group % 32, 31}):
+            assert np.array_equal(np.rint(got[b, h].astype(np.float64) * cnt), exp), (d, p, h)

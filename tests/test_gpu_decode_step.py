@@ -53,9 +53,9 @@ def assert_same_bits(a, b, what):
 @pytest.mark.parametrize("dtype,window,group", [("bf16", 4096, 4), ("bf16", 100, 8), ("bf16", 1, 1),
                                                 ("bf16", 4096, 1), ("bf16", 1000, 1), ("bf16", 300, 2),
                                                 ("f32", 64, 4), ("f32", 5, 1)])
-def test_fused_step_equals_write_then_decode(dtype, window, group):
+@pytest.mark.parametrize("d", [128, 64, 16])
+def test_fused_step_equals_write_then_decode(dtype, window, group, d):
     hkv = 2
-    d = 128 if dtype == "bf16" else 16
     positions = sorted({0, 1, max(0, window - 2), window - 1, window, window + 1, 3 * window + 5, 9000})
     wl = make_workload("step", 70 + window, [(p, 1) for p in positions], window=window, n_q_heads=hkv * group,
                        n_kv_heads=hkv, head_dim=d, dtype=dtype, cache_rows=list(reversed(range(len(positions)))))

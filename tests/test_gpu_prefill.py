@@ -74,9 +74,8 @@ def test_bf16_window_at_least_length_is_causal():
     assert a <= 2e-2 and b <= 2e-2
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_window_one_is_exact(dtype):
-    d = 128 if dtype == "bf16" else 16
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("bf16", 16), ("f32", 16)])
+def test_window_one_is_exact(dtype, d):
     wl = make_workload("w1", 9, [(0, 150), (37, 20)], window=1, n_q_heads=8, n_kv_heads=2, head_dim=d, dtype=dtype)
     cache = poisoned_cache(2, 2, 1, d, dtype)
     write_history(cache, wl)
@@ -85,17 +84,13 @@ def test_window_one_is_exact(dtype):
         assert np.array_equal(got[:, h, :], wl.v_new[:, h // 4, :])
 
 
-@pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("window", [1, 2, 3, 4, 8, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 4096])
-def test_mask_extraction_bf16(window, group):
+def mask_extraction(window, group, d, cases):
     """Q = 0 makes every weight 1/|J(i)|; one-hot V turns O * |J(i)| into the exact
     histogram of the attended positions, so any off-by-one at the window edge or the
-    diagonal shows, also through the ring (history) and the chunk boundary.  Every
-    compiled group size: a workgroup spans 256 / G query positions, so the band
-    loop bounds differ per G."""
-    hkv, d = 2, 128
+    diagonal shows, also through the ring (history) and the chunk boundary."""
+    hkv = 2
     hq = hkv * group
-    for start, n_new in [(0, 300), (200, 190), (5000, 70), (4000, 600)]:
+    for start, n_new in cases:
         hist_lo = max(0, start - window + 1)
         wl = make_workload("mask", 1, [(start, n_new)], window=window, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
                            dtype="bf16")
@@ -108,10 +103,45 @@ def test_mask_extraction_bf16(window, group):
         write_history(cache, wl)
         got = host_f32(run_prefill(wl, cache), "bf16")
         for r in range(n_new):
-            exp, cnt = expected_hist(start + r, window)
-            for h in sorted({0, group - 1, group, hq - 1}):
+            exp, cnt = expected_hist(start + r, window, d)
+            for h in sorted({0, group - 1, group % hq, hq - 1}):
                 hist = np.rint(got[r, h].astype(np.float64) * cnt)
-                assert np.array_equal(hist, exp), (window, start, r, h)
+                assert np.array_equal(hist, exp), (d, window, start, r, h)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("window", [1, 2, 3, 4, 8, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 4096])
+def test_mask_extraction_bf16(window, group):
+    """Every compiled group size: a workgroup spans 256 / G query positions, so the
+    band loop bounds differ per G."""
+    mask_extraction(window, group, 128, [(0, 300), (200, 190), (5000, 70), (4000, 600)])
+
+
+SMALL_D_WINDOWS = [(d, w) for d in (16, 64) for w in (1, 3, 17, 64, 65, 129, 256, 512, 4096)
+                   if not (d == 16 and w > 512)]
+
+
+@pytest.mark.parametrize("group", [1, 4, 8])
+@pytest.mark.parametrize("d,window", SMALL_D_WINDOWS)
+def test_mask_extraction_bf16_small_head_dims(d, window, group):
+    """head_dim 64 (32-position codes) and 16 (8-position codes; their counts reach
+    W / 8, and a bf16 output resolves them exactly only up to W = 512)."""
+    mask_extraction(window, group, d, [(0, 300), (200, 190), (5000, 70), (4000, 300)])
+
+
+@pytest.mark.parametrize("d", [16, 64])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_bf16_small_head_dims_with_history(d, group):
+    hkv = 16 // group if group < 8 else 2
+    for window in (37, 256):
+        prefill_case(700 + d + group + window, [(300, 200), (5, 70), (1000, 1), (0, 129)], window, hkv * group, hkv,
+                     d, "bf16")
+
+
+@pytest.mark.parametrize("d", [16, 64])
+def test_bf16_small_head_dims_long_chunk_through_ring(d):
+    """A 2000-token chunk after 3000 positions of history at W = 1024, 32 q / 8 kv heads."""
+    prefill_case(800 + d, [(3000, 2000), (0, 700)], 1024, 32, 8, d, "bf16")
 
 
 def test_figure3_chunks_through_the_ring():
