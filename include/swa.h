@@ -21,7 +21,9 @@
  *   - Pointers named in the structs and arguments are DEVICE pointers owned by
  *     the caller, except the fields prefixed h_ (host pointers).  The library
  *     allocates nothing, keeps no pointer after returning and has no global
- *     mutable state; calls are re-entrant.
+ *     mutable state; calls are re-entrant.  (The one exception is
+ *     swa_decode_step_noalloc, whose split partials live in a device array of
+ *     the library's own; see there.)
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *     null stream) and never synchronizes.  Buffers must stay alive until the
  *     enqueued work has finished.
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SWA_ABI_VERSION 2  /* 2: swa_decode_step added */
+#define SWA_ABI_VERSION 3  /* 2: swa_decode_step added; 3: swa_decode_step_noalloc */
 
 typedef enum swa_dtype {
   SWA_DTYPE_BF16 = 0, /* bfloat16 storage, fp32 arithmetic, bf16 output (round to nearest even) */
@@ -208,6 +210,29 @@ int swa_decode_step(const swa_cache *cache, const swa_batch *batch,
                     const void *k_new, const void *v_new,
                     float sm_scale, void *out,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * swa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, validation and result
+ * as swa_decode_step -- output and cache bit for bit -- but the split
+ * partials go to a device array inside the library of
+ * SWA_DECODE_WORKSPACE_MAX_BYTES bytes (8 MiB), one per GPU, held until the
+ * process ends.  It calls no allocator.  The first call on a GPU looks up the
+ * array's address (make it outside a graph capture); later calls only
+ * launch.  Limits and hazards:
+ *   - SWA_ERR_WORKSPACE if the plan would need more than the array holds
+ *     (swa_decode_workspace_size() > SWA_DECODE_WORKSPACE_MAX_BYTES; never
+ *     the case for head_dim <= 128);
+ *   - `stream` must belong to the current device (SWA_ERR_INVALID_ARGUMENT);
+ *   - all calls on one GPU share the array: calls that overlap in time on one
+ *     GPU (different streams, or concurrent graph replays) race and give wrong
+ *     results.  Calls ordered on one stream are safe.
+ */
+int swa_decode_step_noalloc(const swa_cache *cache, const swa_batch *batch,
+                            const void *q, int32_t n_q_heads,
+                            const void *k_new, const void *v_new,
+                            float sm_scale, void *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ __all__ = [
     "SWA_ERR_WORKSPACE", "SWA_ERR_HIP", "SWA_ERR_INTERNAL", "SwaError", "SwaLibraryMissing",
     "SwaCacheC", "SwaBatchC", "Cache", "Batch", "lib", "lib_path",
     "swa_abi_version", "swa_status_string", "swa_cache_write", "swa_prefill_chunk",
-    "swa_decode_workspace_size", "swa_decode", "swa_decode_step",
+    "swa_decode_workspace_size", "swa_decode", "swa_decode_step", "swa_decode_step_noalloc",
 ]
 
 SWA_DTYPE_BF16 = 0
@@ -97,6 +97,10 @@ def lib():
     L.swa_decode_step.argtypes = [P(SwaCacheC), P(SwaBatchC), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
+    L.swa_decode_step_noalloc.restype = ctypes.c_int
+    L.swa_decode_step_noalloc.argtypes = [P(SwaCacheC), P(SwaBatchC), ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                          ctypes.c_void_p]
     _lib = L
     return L
 
@@ -253,3 +257,12 @@ def swa_decode_step(cache, batch, q, n_q_heads: int, k_new, v_new, sm_scale: flo
                                  _ptr(v_new), float(sm_scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
                                  _stream(stream))
     return _check(code, "swa_decode_step") if check else code
+
+
+def swa_decode_step_noalloc(cache, batch, q, n_q_heads: int, k_new, v_new, sm_scale: float, out, stream=None,
+                            check: bool = True) -> int:
+    """swa_decode_step with the split partials in the library's own device array (no workspace argument)."""
+    c, b = _as_cache(cache), _as_batch(batch)
+    code = lib().swa_decode_step_noalloc(ctypes.byref(c), ctypes.byref(b), _ptr(q), int(n_q_heads), _ptr(k_new),
+                                         _ptr(v_new), float(sm_scale), _ptr(out), _stream(stream))
+    return _check(code, "swa_decode_step_noalloc") if check else code

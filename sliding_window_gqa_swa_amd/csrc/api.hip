@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/swa.h"
@@ -200,6 +201,42 @@ static int decode_impl(const swa_cache *cache, const swa_batch *batch, const voi
 
 }  // namespace swa
 
+// Split partials of swa_decode_step_noalloc, for callers that cannot allocate
+// device memory.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU shares it.  The decode kernels write
+// every partial they later read, so nothing needs to start at zero.
+static __device__ __align__(256) unsigned char scratch[SWA_DECODE_WORKSPACE_MAX_BYTES];
+
+namespace swa {
+
+constexpr int kMaxDevices = 1024;
+static std::mutex g_scratch_mutex;
+static void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current GPU's copy of `scratch`.  In host code the
+// array's name is only a host-side handle, so the address is looked up once
+// per device, with that device current, and only this pointer reaches kernels.
+static swa_status scratch_of_current_device(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SWA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SWA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SWA_ERR_HIP;
+    if ((int)sdev != dev) return SWA_ERR_INVALID_ARGUMENT;  // the stream must belong to the current device
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SWA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SWA_OK;
+}
+
+}  // namespace swa
+
 using namespace swa;
 
 extern "C" {
@@ -313,6 +350,34 @@ int swa_decode_step(const swa_cache *cache, const swa_batch *batch, const void *
     if (!k_new || !v_new) return SWA_ERR_INVALID_ARGUMENT;
     return decode_impl(cache, batch, q, n_q_heads, k_new, v_new, sm_scale, out, workspace, workspace_bytes,
                        (hipStream_t)stream);
+  } catch (...) {
+    return SWA_ERR_INTERNAL;
+  }
+}
+
+int swa_decode_step_noalloc(const swa_cache *cache, const swa_batch *batch, const void *q, int32_t n_q_heads,
+                            const void *k_new, const void *v_new, float sm_scale, void *out, void *stream) {
+  try {
+    if (!k_new || !v_new) return SWA_ERR_INVALID_ARGUMENT;
+    // the validation of swa_decode_step, before the scratch is looked up
+    swa_status st = check_cache(cache, true);
+    if (st != SWA_OK) return st;
+    st = check_heads(cache, n_q_heads);
+    if (st != SWA_OK) return st;
+    st = check_batch(batch, cache, true, true);
+    if (st != SWA_OK) return st;
+    if (!scale_ok(sm_scale)) return SWA_ERR_INVALID_ARGUMENT;
+    if (batch->num_seqs == 0) return SWA_OK;
+    if (!q || !out || !aligned16(q) || !aligned16(out) || !aligned16(k_new) || !aligned16(v_new))
+      return SWA_ERR_INVALID_ARGUMENT;
+    const size_t need = swa_decode_workspace_size(cache, batch->num_seqs, n_q_heads);
+    if (need > SWA_DECODE_WORKSPACE_MAX_BYTES) return SWA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+      st = scratch_of_current_device((hipStream_t)stream, &ws);
+      if (st != SWA_OK) return st;
+    }
+    return decode_impl(cache, batch, q, n_q_heads, k_new, v_new, sm_scale, out, ws, need, (hipStream_t)stream);
   } catch (...) {
     return SWA_ERR_INTERNAL;
   }

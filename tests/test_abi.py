@@ -25,7 +25,8 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["swa_abi_version", "swa_status_string", "swa_cache_write", "swa_prefill_chunk",
-                            "swa_decode_workspace_size", "swa_decode", "swa_decode_step"])
+                            "swa_decode_workspace_size", "swa_decode", "swa_decode_step",
+                            "swa_decode_step_noalloc"])
     lib = swa.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -36,7 +37,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     text = open(HEADER).read()
-    assert swa.swa_abi_version() == int(re.search(r"#define SWA_ABI_VERSION (\d+)", text).group(1)) == 2
+    assert swa.swa_abi_version() == int(re.search(r"#define SWA_ABI_VERSION (\d+)", text).group(1)) == 3
     for code in range(6):
         s = swa.swa_status_string(code)
         assert s and isinstance(s, str)
@@ -178,6 +179,28 @@ def test_decode_step_argument_checks():
     assert step(c, one, kn=FAKE + 8, ws=FAKE, wsb=need) == INVALID
     assert step(c, HostBatch([1, 1], [5, 9], rows=[3, 3]), ws=FAKE, wsb=need) == INVALID
     assert step(c, HostBatch([], [])) == swa.SWA_OK
+
+
+def step_noalloc(c, b, hq=32, scale=0.088, q=FAKE, kn=FAKE, vn=FAKE, out=FAKE):
+    return swa.swa_decode_step_noalloc(c, b.c, q, hq, kn, vn, scale, out, stream=0, check=False)
+
+
+def test_decode_step_noalloc_argument_checks():
+    """Rejected on the host like swa_decode_step (before the library's device array is looked up)."""
+    c = cache(window=4096)
+    one = HostBatch([1, 1], [5, 9])
+    assert step_noalloc(c, HostBatch([2, 1], [5, 9])) == INVALID
+    assert step_noalloc(c, one, hq=33) == INVALID
+    assert step_noalloc(c, one, hq=8 * 16) == UNSUPPORTED
+    assert step_noalloc(c, one, scale=0.0) == INVALID
+    assert step_noalloc(cache(v=None, window=4096), one) == INVALID
+    assert step_noalloc(c, one, kn=None) == INVALID
+    assert step_noalloc(c, one, vn=None) == INVALID
+    assert step_noalloc(c, one, kn=FAKE + 8) == INVALID
+    assert step_noalloc(c, one, q=None) == INVALID
+    assert step_noalloc(c, HostBatch([1, 1], [5, 9], rows=[3, 3])) == INVALID
+    assert step_noalloc(c, HostBatch([1], [-4])) == INVALID
+    assert step_noalloc(c, HostBatch([], [])) == swa.SWA_OK
 
 
 def test_workspace_plan():
