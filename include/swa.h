@@ -156,6 +156,22 @@ int swa_prefill_chunk(const swa_cache *cache, const swa_batch *batch,
                       float sm_scale, void *out, void *stream);
 
 /*
+ * Measurement aid for the tile skip of swa_prefill_chunk (paragraph "Sliding
+ * Window Attention": the window cuts the work per token to W keys, which the
+ * paper credits for its speed-up over standard attention at 16K tokens).
+ * Same arguments and the same result, bit for bit, as swa_prefill_chunk, but
+ * every key tile from position 0 up to the query tile is visited -- the whole
+ * causal triangle, as attention without the band skip computes it -- and the
+ * keys outside each query's window are masked.  Keys below the band are read
+ * where the call holds them (positions >= max(0, start_pos - W + 1)).
+ * SWA_DTYPE_BF16 only (SWA_ERR_UNSUPPORTED for SWA_DTYPE_F32).
+ */
+int swa_prefill_chunk_no_tile_skip(const swa_cache *cache, const swa_batch *batch,
+                                   const void *q, int32_t n_q_heads,
+                                   const void *k_new, const void *v_new,
+                                   float sm_scale, void *out, void *stream);
+
+/*
  * Bytes of device workspace swa_decode and swa_decode_step need for this cache
  * shape, batch size and head count (0 when the plan needs none).  Returns 0 for
  * invalid input.  The plan may split each sequence's window into S parts that

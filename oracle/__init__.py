@@ -63,12 +63,19 @@ def _load():
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.swa_oracle_num_threads.restype = ctypes.c_int
     lib.swa_oracle_num_threads.argtypes = []
+    lib.swa_oracle_set_num_threads.restype = None
+    lib.swa_oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
 
 def num_threads() -> int:
     return _load().swa_oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following oracle calls (timing only; results do not depend on it)."""
+    _load().swa_oracle_set_num_threads(int(n))
 
 
 def attend(q, q_pos, k, v, kv_pos0: int, window: int, scale: float) -> np.ndarray:

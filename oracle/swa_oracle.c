@@ -163,6 +163,17 @@ int swa_oracle_ring_write(unsigned char *ring, int n_cache, int n_kv_heads,
     return ORACLE_OK;
 }
 
+/* Threads for the following oracle calls (CPU timings at a stated thread count). */
+void swa_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of threads the OpenMP runtime will use (reported with CPU timings). */
 int swa_oracle_num_threads(void)
 {

@@ -22,7 +22,7 @@ __all__ = [
     "SWA_DTYPE_BF16", "SWA_DTYPE_F32", "SWA_OK", "SWA_ERR_INVALID_ARGUMENT", "SWA_ERR_UNSUPPORTED",
     "SWA_ERR_WORKSPACE", "SWA_ERR_HIP", "SWA_ERR_INTERNAL", "SwaError", "SwaLibraryMissing",
     "SwaCacheC", "SwaBatchC", "Cache", "Batch", "lib", "lib_path",
-    "swa_abi_version", "swa_status_string", "swa_cache_write", "swa_prefill_chunk",
+    "swa_abi_version", "swa_status_string", "swa_cache_write", "swa_prefill_chunk", "swa_prefill_chunk_no_tile_skip",
     "swa_decode_workspace_size", "swa_decode", "swa_decode_step", "swa_decode_step_noalloc",
 ]
 
@@ -88,6 +88,8 @@ def lib():
     L.swa_prefill_chunk.argtypes = [P(SwaCacheC), P(SwaBatchC), ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                                     ctypes.c_void_p]
+    L.swa_prefill_chunk_no_tile_skip.restype = ctypes.c_int
+    L.swa_prefill_chunk_no_tile_skip.argtypes = L.swa_prefill_chunk.argtypes
     L.swa_decode_workspace_size.restype = ctypes.c_size_t
     L.swa_decode_workspace_size.argtypes = [P(SwaCacheC), ctypes.c_int32, ctypes.c_int32]
     L.swa_decode.restype = ctypes.c_int
@@ -229,6 +231,17 @@ def swa_prefill_chunk(cache, batch, q, n_q_heads: int, k_new, v_new, sm_scale: f
     code = lib().swa_prefill_chunk(ctypes.byref(c), ctypes.byref(b), _ptr(q), int(n_q_heads), _ptr(k_new),
                                    _ptr(v_new), float(sm_scale), _ptr(out), _stream(stream))
     return _check(code, "swa_prefill_chunk") if check else code
+
+
+def swa_prefill_chunk_no_tile_skip(cache, batch, q, n_q_heads: int, k_new, v_new, sm_scale: float, out,
+                                   stream=None, check: bool = True) -> int:
+    """swa_prefill_chunk without the band tile skip (every causal key tile visited, out-of-band keys
+    masked): same result, for measuring what the skip saves."""
+    c, b = _as_cache(cache), _as_batch(batch)
+    code = lib().swa_prefill_chunk_no_tile_skip(ctypes.byref(c), ctypes.byref(b), _ptr(q), int(n_q_heads),
+                                                _ptr(k_new), _ptr(v_new), float(sm_scale), _ptr(out),
+                                                _stream(stream))
+    return _check(code, "swa_prefill_chunk_no_tile_skip") if check else code
 
 
 def swa_decode_workspace_size(cache, num_seqs: int, n_q_heads: int) -> int:

@@ -279,8 +279,12 @@ int swa_cache_write(const swa_cache *cache, const swa_batch *batch, const void *
   }
 }
 
-int swa_prefill_chunk(const swa_cache *cache, const swa_batch *batch, const void *q, int32_t n_q_heads,
-                      const void *k_new, const void *v_new, float sm_scale, void *out, void *stream) {
+}  // extern "C"
+
+// swa_prefill_chunk, and (visit_all_tiles) its measurement variant without the band tile skip.
+static int prefill_impl(const swa_cache *cache, const swa_batch *batch, const void *q, int32_t n_q_heads,
+                        const void *k_new, const void *v_new, float sm_scale, void *out, void *stream,
+                        bool visit_all_tiles) {
   try {
     swa_status st = check_cache(cache, false);
     if (st != SWA_OK) return st;
@@ -308,6 +312,7 @@ int swa_prefill_chunk(const swa_cache *cache, const swa_batch *batch, const void
     p.n_q_heads = n_q_heads;
     p.sm_scale = sm_scale;
     p.scale_log2 = sm_scale * 1.4426950408889634f;
+    p.visit_all_tiles = visit_all_tiles ? 1 : 0;
     hipError_t e;
     if (cache->dtype == SWA_DTYPE_BF16) {
       const int group = n_q_heads / cache->n_kv_heads;
@@ -319,12 +324,26 @@ int swa_prefill_chunk(const swa_cache *cache, const swa_batch *batch, const void
       p.n_work = (int32_t)n_work;
       e = launch_prefill_bf16(p, group, (hipStream_t)stream);
     } else {
+      if (visit_all_tiles) return SWA_ERR_UNSUPPORTED;  // the fp32 path has no key tiles
       e = launch_prefill_f32(p, (hipStream_t)stream);
     }
     return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
   } catch (...) {
     return SWA_ERR_INTERNAL;
   }
+}
+
+extern "C" {
+
+int swa_prefill_chunk(const swa_cache *cache, const swa_batch *batch, const void *q, int32_t n_q_heads,
+                      const void *k_new, const void *v_new, float sm_scale, void *out, void *stream) {
+  return prefill_impl(cache, batch, q, n_q_heads, k_new, v_new, sm_scale, out, stream, false);
+}
+
+int swa_prefill_chunk_no_tile_skip(const swa_cache *cache, const swa_batch *batch, const void *q,
+                                   int32_t n_q_heads, const void *k_new, const void *v_new, float sm_scale,
+                                   void *out, void *stream) {
+  return prefill_impl(cache, batch, q, n_q_heads, k_new, v_new, sm_scale, out, stream, true);
 }
 
 size_t swa_decode_workspace_size(const swa_cache *cache, int32_t num_seqs, int32_t n_q_heads) {

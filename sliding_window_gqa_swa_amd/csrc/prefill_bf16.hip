@@ -45,8 +45,11 @@
 //         a weight is exp2(c * accumulator), one multiply per score;
 //       - the row sums are an MFMA of the bf16 weights with a ones operand,
 //         which also leaves every lane with its query's complete sum;
-//       - the rescale test is one compare of the tile max against a per-row
-//         threshold.
+//       - the rescale test is one compare of each lane's tile max against
+//         the row's threshold; the cross-lane row max is only formed on the
+//         rare tiles that rescale;
+//       - the unmasked interior loop is unrolled by 6 (3 K slots x 2 V slots),
+//         so LDS slot addresses are immediate offsets.
 //   * Work order (KV head, sequence, query tile from the last), dealt to the
 //     XCDs in contiguous ranges: one KV head per XCD balances ragged batches
 //     and keeps each head's K/V in one L2.
@@ -138,7 +141,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   // (positions go up to 2^31 - 1: sums that may pass it are formed in 64 bits)
   const int hi = q0 + min(kBQ, q_end - q0) - 1;   // last key any row needs
   const int lo = max(0, q0 - W + 1);              // first key any row needs
-  const int kt0 = (lo / kBN) * kBN;
+  // Measurement variant without the band tile skip (visit_all_tiles): the
+  // tiles start at key 0, as in attention that visits the whole causal
+  // triangle and masks; keys below the band are read where the call holds
+  // them (from max(0, s - W + 1) on) and masked.  Same result.
+  const int kt0 = p.visit_all_tiles ? 0 : (lo / kBN) * kBN;
+  const int lo_rd = p.visit_all_tiles ? max(0, s - W + 1) : lo;  // first key row that may be read
   const int n_tiles = (hi - kt0) / kBN + 1;
   // tiles starting at or after nomask_lo (and ending by q0) need no mask
   const int64_t nomask_lo = (int64_t)q0 + kBQ - W;
@@ -185,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const uint32_t lane_off_ring = (uint32_t)(row_l * kRowB + lchunk * 16);
   auto load_tile = [&](unsigned char *dst, int ts) __attribute__((always_inline)) {
     if (Gm::kNL < 4 && wg >= Gm::kNL) return;  // D = 16: a tile is two loads
-    const bool all_valid = ts >= lo && ts + kBN - 1 <= hi;
+    const bool all_valid = ts >= lo_rd && ts + kBN - 1 <= hi;
     const int ts_mod = ts % W;
     // fast paths: a uniform base (scalar registers) plus this lane's 32-bit offset
     if (all_valid && ts >= s) {
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
       // edge tile: rows outside [lo, hi] read the nearest key of the band
 #pragma unroll
       for (int m = 0; m < Gm::kLoads; m++) {
-        const int j = min(max(ts + row_l + 4 * kRpl * m, lo), hi);
+        const int j = min(max(ts + row_l + 4 * kRpl * m, lo_rd), hi);
         const char *src = j < s ? src_ring + (ring_row0 + j % W) * kRowB
                                 : src_new + ((new_tok0 + j) * hkv + g) * (int64_t)kRowB;
         __builtin_amdgcn_global_load_lds(src + lchunk * 16, (lds_void *)(dst + (wg + 4 * m) * 1024), 16, 0, 0);
@@ -336,9 +344,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
       for (int e = 2; e < 16; e += 2)
         mt = fmaxf(fmaxf(mt, sa[e / 4][qb][e % 4]), sa[e / 4][qb][e % 4 + 1]);
-      mt = max_pair32(max_pair16(mt));
-      const bool upd = mt > gap[qb];
-      if (__builtin_amdgcn_ballot_w64(upd)) {
+      // The test runs on each lane's own 16 values: the 4 lanes of a query
+      // share its threshold, so the query's max exceeds it iff one of its
+      // lanes does.  The cross-lane max is only formed on the rare tiles that
+      // rescale.
+      if (__builtin_amdgcn_ballot_w64(mt > gap[qb])) {
+        mt = max_pair32(max_pair16(mt));
+        const bool upd = mt > gap[qb];
         const bool m_inf = gap[qb] == -INFINITY;
         const float mc = -negm[qb][0];
         const float mn = upd ? mt + mc : (m_inf ? -INFINITY : mc);
@@ -408,23 +420,30 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma - 2 * kPairs, 0);
   };
 
-  auto step = [&](int t, bool masked, auto with_qk) __attribute__((always_inline)) {
+  // One tile: t is the tile index; R = t mod 6 when it is known at compile
+  // time (then every LDS slot address is a constant offset), -1 otherwise.
+  auto step_r = [&](int t, bool masked, auto with_qk, auto res) __attribute__((always_inline)) {
+    constexpr int R = decltype(res)::value;
     const int nt = grp == 0 ? t + 2 : t + 1;  // the tile this group streams now
-    if (nt < n_tiles) load_tile(grp == 0 ? kslot(nt % 3) : vslot(nt & 1), kt0 + nt * kBN);
+    const int kl = R < 0 ? (t + 2) % 3 : (R + 2) % 3, vl = R < 0 ? (t + 1) & 1 : (R + 1) & 1;
+    const int kq = R < 0 ? (t + 1) % 3 : (R + 1) % 3, vp = R < 0 ? t & 1 : R & 1;
+    if (nt < n_tiles) load_tile(grp == 0 ? kslot(kl) : vslot(vl), kt0 + nt * kBN);
     softmax(kt0 + t * kBN, masked);
     wait_vmem();
     __syncthreads();
     // the matrix half-step's wave issues first when both waves of the SIMD are
     // ready (MFMAs and operand reads ahead of the other wave's softmax VALU)
     __builtin_amdgcn_s_setprio(3);
-    pv(vslot(t & 1));
+    pv(vslot(vp));
     if constexpr (decltype(with_qk)::value) {
-      qk(kslot((t + 1) % 3));
+      qk(kslot(kq));
       schedule_matrix_half_step();
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   };
+  constexpr std::integral_constant<int, -1> kRt{};
+  auto step = [&](int t, bool masked, auto with_qk) __attribute__((always_inline)) { step_r(t, masked, with_qk, kRt); };
 
   if (grp == 0) {
     load_tile(kslot(0), kt0);
@@ -442,7 +461,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int t_last = n_tiles - 1;
   int t = 0;
   for (; t < min(n_lead, t_last); t++) step(t, true, kNext);
-  for (; t < min(t_mid_end, t_last); t++) step(t, false, kNext);
+  {
+    // the unmasked interior, unrolled by 6 (3 K slots x 2 V slots) from a tile
+    // index that is a multiple of 6, so its slot addresses are immediates
+    const int mid_end = min(t_mid_end, t_last);
+    for (; t < mid_end && t % 6 != 0; t++) step(t, false, kNext);
+    for (; t + 6 <= mid_end; t += 6) {
+      step_r(t, false, kNext, std::integral_constant<int, 0>{});
+      step_r(t + 1, false, kNext, std::integral_constant<int, 1>{});
+      step_r(t + 2, false, kNext, std::integral_constant<int, 2>{});
+      step_r(t + 3, false, kNext, std::integral_constant<int, 3>{});
+      step_r(t + 4, false, kNext, std::integral_constant<int, 4>{});
+      step_r(t + 5, false, kNext, std::integral_constant<int, 5>{});
+    }
+    for (; t < mid_end; t++) step(t, false, kNext);
+  }
   for (; t < t_last; t++) step(t, true, kNext);
   step(t_last, !(t_last >= n_lead && t_last < t_mid_end), kLast);
   if (grp == 0) __builtin_amdgcn_s_barrier();  // group A: matches B's extra barrier

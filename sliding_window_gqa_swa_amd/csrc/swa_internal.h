@@ -51,6 +51,7 @@ struct PrefillParams {
   int32_t n_work;         // num_seqs * tiles_per_seq * n_kv_heads
   float scale_log2;       // sm_scale * log2(e)
   float sm_scale;
+  int32_t visit_all_tiles;  // measurement variant: no band tile skip (bf16 prefill)
 };
 
 struct DecodeParams {

@@ -26,7 +26,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["swa_abi_version", "swa_status_string", "swa_cache_write", "swa_prefill_chunk",
                             "swa_decode_workspace_size", "swa_decode", "swa_decode_step",
-                            "swa_decode_step_noalloc"])
+                            "swa_decode_step_noalloc", "swa_prefill_chunk_no_tile_skip"])
     lib = swa.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -130,6 +130,18 @@ def test_bad_batch_metadata():
     assert write(c, HostBatch([3], [0], num_seqs=-1)) == INVALID
     assert write(c, HostBatch([3], [0]), kn=None) == INVALID
     assert write(c, HostBatch([3], [0]), vn=FAKE + 2) == INVALID
+
+
+def test_no_tile_skip_variant_checks():
+    c = cache()
+    b = HostBatch([10, 4], [0, 3])
+    nts = lambda cc, bb, **kw: swa.swa_prefill_chunk_no_tile_skip(cc, bb.c, kw.get("q", FAKE), kw.get("hq", 32),
+                                                                  FAKE, FAKE, 0.088, FAKE, stream=0, check=False)
+    assert nts(c, b, hq=12) == INVALID
+    assert nts(c, b, q=None) == INVALID
+    assert nts(cache(dtype=swa.SWA_DTYPE_F32, head_dim=16), HostBatch([3], [-1])) == INVALID
+    assert nts(cache(dtype=swa.SWA_DTYPE_F32, head_dim=16), HostBatch([3], [0])) == UNSUPPORTED
+    assert nts(c, HostBatch([], [])) == swa.SWA_OK
 
 
 def test_prefill_argument_checks():

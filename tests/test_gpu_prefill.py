@@ -231,3 +231,24 @@ def test_positions_next_to_int32_max(dtype):
 
 def test_empty_sequence_inside_a_batch():
     prefill_case(92, [(0, 130), (40, 0), (500, 77), (3, 0)], 64, 32, 8, 128, "bf16")
+
+
+@pytest.mark.parametrize("group,d", [(4, 128), (1, 128), (8, 128), (4, 64), (2, 16)])
+def test_no_tile_skip_variant_is_bitwise_identical(group, d):
+    """swa_prefill_chunk_no_tile_skip visits every key tile from position 0 and
+    masks the keys outside the window; the extra keys get weight exactly 0, so
+    the output equals swa_prefill_chunk bit for bit (and matches the oracle)."""
+    hkv = 2
+    wl = make_workload("noskip", 40 + group + d, [(0, 1500), (3000, 700), (100, 33)], window=256,
+                       n_q_heads=hkv * group, n_kv_heads=hkv, head_dim=d, dtype="bf16")
+    cache = poisoned_cache(wl.n_cache, hkv, 256, d, "bf16")
+    write_history(cache, wl)
+    ref = run_prefill(wl, cache)
+    q, kn, vn = dev(wl.q, "bf16"), dev(wl.k_new, "bf16"), dev(wl.v_new, "bf16")
+    out = empty((wl.total_tokens, wl.n_q_heads, d), "bf16")
+    out.fill_(float("nan"))
+    swa.swa_prefill_chunk_no_tile_skip(cache, new_batch(wl), q, wl.n_q_heads, kn, vn, wl.scale, out)
+    t = torch()
+    t.cuda.synchronize()
+    assert t.equal(out.view(t.int16), ref.view(t.int16))
+    check_close(host_f32(out, "bf16"), oracle_all(wl), "bf16", "no tile skip")

@@ -321,3 +321,16 @@ def test_cache_memory_stops_at_window():
     # theoretical attention span of the last layer for 32 layers (the paper's ~131K)
     assert 32 * window == 131072
     assert 32 * (window - 1) == 131040
+
+
+def test_thread_count_does_not_change_results():
+    """The oracle computes each (query, head) in one thread, in a fixed order: its
+    results are bitwise the same at any thread count (the CPU baseline is timed at
+    several)."""
+    rng = np.random.default_rng(21)
+    q, k, v = rnd(rng, (40, 4, 16)), rnd(rng, (40, 2, 16)), rnd(rng, (40, 2, 16))
+    oracle.set_num_threads(1)
+    a = oracle.attend(q, np.arange(40), k, v, 0, 9, 0.3)
+    oracle.set_num_threads(max(2, os.cpu_count() or 2))
+    b = oracle.attend(q, np.arange(40), k, v, 0, 9, 0.3)
+    assert np.array_equal(a, b)
