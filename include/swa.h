@@ -5,7 +5,7 @@
  * What is computed (Mistral 7B (Chinese translation), section 2
  * "Architectural details"):
  *   - paragraph "Sliding Window Attention" and the Figure 1 caption: the token
- *     at position i attends to the W positions i-W+1 .. i (at most W tokens,
+ *     at position i attends to the W positions i-W+1 .. i (no more than W,
  *     ending at itself; positions below 0 do not exist);
  *   - section 1 "Introduction": grouped-query attention; here query head h
  *     reads key/value head h / G with G = n_q_heads / n_kv_heads;

@@ -84,7 +84,7 @@ def attend(q, q_pos, k, v, kv_pos0: int, window: int, scale: float) -> np.ndarra
     q: float32 [n_q, Hq, D] (exact input values); q_pos: int64 [n_q]
     k, v: float32 [n_kv, Hkv, D]; row t is absolute position ``kv_pos0 + t``
     Returns float64 [n_q, Hq, D].  Query position i attends to keys
-    j in [max(0, i-W+1), i] (W keys, the reading of "at most W tokens").
+    j in [max(0, i-W+1), i] (W keys: the Figure 1 caption bounds the window by W tokens).
     """
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)

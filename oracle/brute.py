@@ -6,8 +6,8 @@ used to pin the C oracle on tiny inputs.  It builds the explicit N x N mask
     M[i, j] = (j <= i) and (i - j < W)
 
 (Mistral 7B (Chinese translation), section 2, paragraph "Sliding Window
-Attention" and the Figure 1 caption: at most W tokens, ending at the query
-itself), sets masked scores to -inf, takes a dense row softmax and multiplies
+Attention" and the Figure 1 caption: a window of W tokens ending at the
+query itself), sets masked scores to -inf, takes a dense row softmax and multiplies
 by V.  Query head h reads key/value head h // G (grouped-query attention,
 section 1).
 """

@@ -19,8 +19,9 @@
  *
  * Readings taken where the pages leave a step open (listed in full in the
  * design notes of the repository):
- *   - window: W keys, positions j with i-W < j <= i (the caption's "at most W
- *     tokens"; a W-slot ring holds exactly these after writing position i);
+ *   - window: W keys, positions j with i-W < j <= i (the caption bounds the
+ *     window by W tokens; a W-slot ring holds exactly these after writing
+ *     position i);
  *   - GQA grouping: query head h uses key/value head floor(h / G), G = Hq/Hkv;
  *   - softmax scale: passed in by the caller (1/sqrt(head_dim) by default);
  *   - positions are 0-based, so the first overwrite happens at i = W.
