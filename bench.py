@@ -13,7 +13,15 @@ The headline value is the prefill's band TFLOP/s (algorithmic FLOPs: 4 * D *
 Hq * sum_i |J(i)|); the decode's K/V GB/s is reported beside it.  Each stage
 is timed with HIP events on the stream it runs on.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+The suite (default on) times the other workloads: causal attention and the
+prefill without its band tile skip at 16K tokens, 4 x 32768 tokens chunked
+through the ring (and a chunk-size sweep), the ragged mixed batch, decode at
+G = 1, per-token decode steps, and a 32-layer ring.  The CPU baseline is the
+fp64 oracle on the host cores: the whole 16K prefill, plus stated samples of
+the other workloads.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-suite]
+    python bench.py --only chunked|mixed|decode_g1   # one suite workload (for profilers)
 """
 from __future__ import annotations
 
@@ -34,6 +42,8 @@ SPEC_CLOCK_GHZ = 2.4        # the clock the MFMA peak is quoted at
 PREFILL_KERNEL = "prefill_bf16_kernel"
 PMC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_mistral16k_w4096_pmc.json")
 PREFILL_SRC = os.path.join(ROOT, "sliding_window_gqa_swa_amd", "csrc", "prefill_bf16.hip")
+W = 4096
+HQ, HKV, D = 32, 8, 128
 
 
 def band_pairs(start: int, n: int, window: int) -> int:
@@ -60,6 +70,11 @@ def pmc_record():
     return rec
 
 
+def pmc_source() -> str:
+    return (f"read from {os.path.relpath(PMC_FILE, ROOT)} (rocprofv3 counters of an earlier run; used only while "
+            f"the prefill source sha256[:16] {src_digest(PREFILL_SRC)} matches the one recorded there)")
+
+
 def pmc_traffic():
     """HBM bytes per prefill launch (calibrated FETCH_SIZE + WRITE_SIZE), or None."""
     rec = pmc_record()
@@ -77,36 +92,147 @@ def sclk_estimate(t_launch_ms: float, tflops: float):
     peak_at_clk = PEAK_BF16_TFLOPS * ghz / SPEC_CLOCK_GHZ
     return {"ghz": round(ghz, 3), "spec_ghz": SPEC_CLOCK_GHZ, "mfma_peak_at_sclk_tflops": round(peak_at_clk, 1),
             "frac_of_peak_at_sclk": round(tflops / peak_at_clk, 4),
-            "source": "GRBM_GUI_ACTIVE cycles per launch / 8 XCDs / the launch's measured duration"}
+            "source": "GRBM_GUI_ACTIVE cycles per launch / 8 XCDs / this run's measured launch duration; the "
+                      "cycle count is " + pmc_source()}
 
 
-def cpu_baseline(wl, sample_rows: int):
-    """The fp64 oracle on a bounded, evenly spaced sample of the prefill's query rows."""
+# ----------------------------------------------------------------------------- CPU baseline (the oracle)
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def oracle_timed(fn, threads: int, min_s: float = 0.0):
+    """Seconds per call of fn (an oracle call) at `threads` OpenMP threads.  Calls
+    shorter than min_s are repeated and averaged."""
+    import oracle
+    oracle.set_num_threads(threads)
+    used = oracle.num_threads()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            break
+    oracle.set_num_threads(host_threads())
+    return dt / n, used
+
+
+def cpu_baseline_prefill(wl):
+    """The fp64 oracle on every query row of the 16K prefill (W = 4096)."""
     import numpy as np
     import oracle
     from sliding_window_gqa_swa_amd.workloads import to_f32
     n = wl.seqs[0].n_new
-    rows = np.unique(np.linspace(0, n - 1, sample_rows).astype(np.int64))
-    q = to_f32(wl.q[rows], wl.dtype)
-    k = to_f32(wl.k_new, wl.dtype)
-    v = to_f32(wl.v_new, wl.dtype)
-    t0 = time.perf_counter()
-    oracle.attend(q, rows, k, v, 0, wl.window, wl.scale)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * wl.head_dim * wl.n_q_heads * sum(min(int(i) + 1, wl.window) for i in rows)
-    model = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "cpu_model": model,
-            "sample": f"{len(rows)} of the {n} query rows (evenly spaced) x {wl.n_q_heads} heads of the "
-                      f"16384-token prefill (W={wl.window}), fp64, {flops / 1e9:.1f} GFLOP in {dt:.2f} s"}
+    rows = np.arange(n)
+    q, k, v = to_f32(wl.q, wl.dtype), to_f32(wl.k_new, wl.dtype), to_f32(wl.v_new, wl.dtype)
+    dt, used = oracle_timed(lambda: oracle.attend(q, rows, k, v, 0, wl.window, wl.scale), host_threads())
+    flops = 4.0 * wl.head_dim * wl.n_q_heads * band_pairs(0, n, wl.window)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"all {n} query rows x {wl.n_q_heads} heads of the 16384-token prefill (W={wl.window}), "
+                      f"fp64, {flops / 1e9:.1f} GFLOP in {dt:.2f} s"}
 
+
+def cpu_leg_tiny():
+    """Tiny fp32 configuration (1 x 64 tokens, 4 q / 2 kv heads, head_dim 16, W = 8): whole workload."""
+    import numpy as np
+    import oracle
+    from sliding_window_gqa_swa_amd.workloads import tiny_prefill, to_f32
+    wl = tiny_prefill(1001)
+    q, k, v = to_f32(wl.q, "f32"), to_f32(wl.k_new, "f32"), to_f32(wl.v_new, "f32")
+    pos = np.arange(64)
+    flops = 4.0 * 16 * 4 * band_pairs(0, 64, 8)
+    rec = {"workload": "tiny fp32: 1 x 64 tokens, 4 q / 2 kv heads, head_dim 16, W = 8 (whole)", "flops": flops}
+    for th in (host_threads(), 1):
+        dt, used = oracle_timed(lambda: oracle.attend(q, pos, k, v, 0, 8, 0.25), th, min_s=0.5)
+        rec[f"threads_{used}"] = {"s_per_call": dt, "gflops": round(flops / dt / 1e9, 3)}
+    return rec
+
+
+def cpu_leg_decode(wd):
+    """64-sequence decode (full 4096-slot windows): every sequence and head, all threads and one thread."""
+    import numpy as np
+    import oracle
+    from sliding_window_gqa_swa_amd.workloads import to_f32
+    args = []
+    for b, s in enumerate(wd.seqs):
+        kk = np.concatenate([to_f32(wd.hist_k[b], "bf16"), to_f32(wd.k_new[b:b + 1], "bf16")])
+        vv = np.concatenate([to_f32(wd.hist_v[b], "bf16"), to_f32(wd.v_new[b:b + 1], "bf16")])
+        args.append((to_f32(wd.q[b:b + 1], "bf16"), np.array([s.start_pos]), kk, vv, s.hist_lo))
+
+    def run():
+        for q, pos, kk, vv, lo in args:
+            oracle.attend(q, pos, kk, vv, lo, W, wd.scale)
+
+    kv_bytes = sum(2 * HKV * D * 2 * min(s.start_pos + 1, W) for s in wd.seqs)
+    rec = {"workload": f"{wd.num_seqs}-sequence decode, full {W}-slot windows (whole)", "kv_bytes": kv_bytes}
+    for th in (host_threads(), 1):
+        dt, used = oracle_timed(run, th)
+        rec[f"threads_{used}"] = {"s": round(dt, 3), "kv_gbps": round(kv_bytes / dt / 1e9, 3)}
+    return rec
+
+
+def cpu_leg_chunked(q, k, v, b=0, chunk_start=32768 - 4096, chunk=4096):
+    """Chunked 4 x 32768 workload, sample: the last chunk of sequence 0 (every row and head)."""
+    import numpy as np
+    import oracle
+    from sliding_window_gqa_swa_amd.workloads import to_f32
+    rows = np.arange(chunk_start, chunk_start + chunk)
+    lo = chunk_start - W + 1
+    qs = to_f32(q[b, chunk_start:chunk_start + chunk], "bf16")
+    ks, vs = to_f32(k[b, lo:chunk_start + chunk], "bf16"), to_f32(v[b, lo:chunk_start + chunk], "bf16")
+    dt, used = oracle_timed(lambda: oracle.attend(qs, rows, ks, vs, lo, W, 1 / 128 ** 0.5), host_threads())
+    flops = 4.0 * D * HQ * band_pairs(chunk_start, chunk, W)
+    return {"sample": f"sequence {b}, positions {chunk_start}..{chunk_start + chunk - 1} (the last chunk), all heads",
+            "cores": used, "gflop": round(flops / 1e9, 1), "s": round(dt, 2), "tflops": round(flops / dt / 1e12, 4)}
+
+
+def cpu_leg_mixed(wp, wd, rows_per_seq=256):
+    """Ragged mixed batch, sample: every decode sequence, and the last `rows_per_seq`
+    query rows of every prefill sequence."""
+    import numpy as np
+    import oracle
+    from sliding_window_gqa_swa_amd.workloads import to_f32
+
+    def seq_args(wl, b, rows):
+        s = wl.seqs[b]
+        sl = wl.seq_tokens(b)
+        kk = np.concatenate([to_f32(wl.hist_k[b], "bf16"), to_f32(wl.k_new[sl], "bf16")])
+        vv = np.concatenate([to_f32(wl.hist_v[b], "bf16"), to_f32(wl.v_new[sl], "bf16")])
+        return to_f32(wl.q[sl][rows], "bf16"), s.start_pos + rows, kk, vv, s.hist_lo
+
+    args, flops = [], 0.0
+    for wl, per in ((wp, rows_per_seq), (wd, 1)):
+        for b, s in enumerate(wl.seqs):
+            rows = np.arange(max(0, s.n_new - per), s.n_new)
+            args.append(seq_args(wl, b, rows))
+            flops += 4.0 * D * HQ * sum(min(int(s.start_pos + r) + 1, W) for r in rows)
+
+    def run():
+        for q, pos, kk, vv, lo in args:
+            oracle.attend(q, pos, kk, vv, lo, W, wp.scale)
+
+    dt, used = oracle_timed(run, host_threads())
+    return {"sample": f"all {wd.num_seqs} decode sequences and the last {rows_per_seq} query rows of each of the "
+                      f"{wp.num_seqs} prefill sequences, all heads", "cores": used, "gflop": round(flops / 1e9, 2),
+            "s": round(dt, 2), "tflops": round(flops / dt / 1e12, 4)}
+
+
+# ----------------------------------------------------------------------------- timing helpers
 
 def time_ms(fn, reps: int) -> float:
     """Mean milliseconds of `fn` over `reps` launches, HIP events on the current stream."""
@@ -139,120 +265,224 @@ def time_ms_cold(fn, reps: int, flush) -> float:
     return total / reps
 
 
-def suite(up, pq, pk, pv, pout, scale, reps: int):
-    """The other workloads of the path, timed (their parity is covered by the GPU tests)."""
+def uploader(dev):
+    import numpy as np
+    import torch
+
+    def up(raw):
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).to(dev)
+    return up
+
+
+def bf16_cache(n, hkv, window, dev, fill=0.0):
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    return swa.Cache(torch.full((n, hkv, window, D), fill, dtype=torch.bfloat16, device=dev),
+                     torch.full((n, hkv, window, D), fill, dtype=torch.bfloat16, device=dev))
+
+
+def write_history(cache, wl, up):
+    import sliding_window_gqa_swa_amd as swa
+    hb = swa.Batch([s.start_pos - s.hist_lo for s in wl.seqs], [s.hist_lo for s in wl.seqs], wl.cache_idx)
+    swa.swa_cache_write(cache, hb, up(wl.hist_packed("k")), up(wl.hist_packed("v")))
+
+
+# ----------------------------------------------------------------------------- suite
+
+def suite_causal_and_no_skip(pq, pk, pv, pout, scale, t_swa_ms, reps):
+    """The paper's 2x at 16K / W = 4096 against standard attention: the same kernel
+    with W >= N (causal attention), and the W = 4096 prefill with its band tile skip
+    turned off (every key tile of the causal triangle visited, out-of-band keys masked)."""
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    dev = pq.device
+    n = pq.shape[0]
+    b1 = swa.Batch([n], [0], [0])
+    cc = bf16_cache(1, HKV, n, dev)
+    t_causal = time_ms(lambda: swa.swa_prefill_chunk(cc, b1, pq, HQ, pk, pv, scale, pout), reps)
+    del cc
+    c4 = bf16_cache(1, HKV, W, dev)
+    t_noskip = time_ms(lambda: swa.swa_prefill_chunk_no_tile_skip(c4, b1, pq, HQ, pk, pv, scale, pout), reps)
+    causal_flops = 4.0 * D * HQ * band_pairs(0, n, n)
+    band_flops = 4.0 * D * HQ * band_pairs(0, n, W)
+    torch.cuda.synchronize()
+    return {
+        "causal_prefill_16k": {"ms": round(t_causal, 4), "tflops": round(causal_flops / t_causal / 1e9, 1)},
+        "no_tile_skip_prefill_16k_w4096": {
+            "ms": round(t_noskip, 4), "band_tflops": round(band_flops / t_noskip / 1e9, 1),
+            "causal_triangle_tflops": round(causal_flops / t_noskip / 1e9, 1),
+            "note": "W = 4096 result, every key tile of the causal triangle visited and masked outside the band"},
+        "swa_vs_causal_speedup_16k": round(t_causal / t_swa_ms, 3),
+        "swa_vs_no_tile_skip_speedup_16k": round(t_noskip / t_swa_ms, 3),
+        "causal_over_band_pairs_16k": round(band_pairs(0, n, n) / band_pairs(0, n, W), 3),
+    }
+
+
+def suite_chunked(up, scale, reps, cpu: bool):
+    """4 x 32768 tokens through the ring in chunks of 4096 (W = 4096), a chunk-size
+    sweep, and the chunk cache write with a cold Infinity Cache."""
     import numpy as np
     import torch
     import sliding_window_gqa_swa_amd as swa
-    from sliding_window_gqa_swa_amd.workloads import chunked_sequences, ragged_mixed
-    dev = pq.device
-    res = {}
-    # causal attention = the same kernel with W >= N: the paper's "standard attention" at 16K
-    n = pq.shape[0]
-    cc = swa.Cache(torch.zeros((1, 8, n, 128), dtype=torch.bfloat16, device=dev),
-                   torch.zeros((1, 8, n, 128), dtype=torch.bfloat16, device=dev))
-    b1 = swa.Batch([n], [0], [0])
-    t_causal = time_ms(lambda: swa.swa_prefill_chunk(cc, b1, pq, 32, pk, pv, scale, pout), reps)
-    causal_flops = 4.0 * 128 * 32 * band_pairs(0, n, n)
-    res["causal_prefill_16k"] = {"ms": round(t_causal, 4), "tflops": round(causal_flops / t_causal / 1e9, 1)}
-    del cc
-
-    # chunked prefill through the ring: 4 x 32768 tokens in 8 chunks of 4096, W = 4096
-    B, N, C, W = 4, 32768, 4096, 4096
+    from sliding_window_gqa_swa_amd.workloads import chunked_sequences
+    dev = torch.device("cuda:0")
+    B, N, C = 4, 32768, 4096
     q, k, v = chunked_sequences(1003, batch=B, n=N, window=W)
     qd, kd, vd = up(q), up(k), up(v)
-    del q, k, v
-    cache = swa.Cache(torch.zeros((B, 8, W, 128), dtype=torch.bfloat16, device=dev),
-                      torch.zeros((B, 8, W, 128), dtype=torch.bfloat16, device=dev))
-    oc = torch.empty((B * C, 32, 128), dtype=torch.bfloat16, device=dev)
+    cache = bf16_cache(B, HKV, W, dev)
+    oc = torch.empty((B * C, HQ, D), dtype=torch.bfloat16, device=dev)
     chunks = []
     for s in range(0, N, C):
         batch = swa.Batch([C] * B, [s] * B, list(range(B)))
-        qc = qd[:, s:s + C].reshape(B * C, 32, 128).contiguous()
-        kc = kd[:, s:s + C].reshape(B * C, 8, 128).contiguous()
-        vc = vd[:, s:s + C].reshape(B * C, 8, 128).contiguous()
-        t_p = time_ms(lambda: swa.swa_prefill_chunk(cache, batch, qc, 32, kc, vc, scale, oc), reps)
+        qc = qd[:, s:s + C].reshape(B * C, HQ, D).contiguous()
+        kc = kd[:, s:s + C].reshape(B * C, HKV, D).contiguous()
+        vc = vd[:, s:s + C].reshape(B * C, HKV, D).contiguous()
+        t_p = time_ms(lambda: swa.swa_prefill_chunk(cache, batch, qc, HQ, kc, vc, scale, oc), reps)
         t_w = time_ms(lambda: swa.swa_cache_write(cache, batch, kc, vc), reps)
-        fl = 4.0 * 128 * 32 * B * band_pairs(s, C, W)
-        chunks.append((t_p, t_w, fl))
-    # chunk-size sweep over the same sequences (the pages advise chunk = window):
-    # prefill + cache write of all chunks, and the activation buffers one call needs
+        chunks.append((t_p, t_w, 4.0 * D * HQ * B * band_pairs(s, C, W)))
     sweep = {}
     for cs in (W // 4, W // 2, W, 2 * W):
         cache.k.zero_()
         cache.v.zero_()
         t_tot, w_tot = 0.0, 0.0
-        ob = torch.empty((B * cs, 32, 128), dtype=torch.bfloat16, device=dev)
+        ob = torch.empty((B * cs, HQ, D), dtype=torch.bfloat16, device=dev)
         for s in range(0, N, cs):
             batch = swa.Batch([cs] * B, [s] * B, list(range(B)))
-            qc = qd[:, s:s + cs].reshape(B * cs, 32, 128).contiguous()
-            kc = kd[:, s:s + cs].reshape(B * cs, 8, 128).contiguous()
-            vc = vd[:, s:s + cs].reshape(B * cs, 8, 128).contiguous()
-            t_tot += time_ms(lambda: swa.swa_prefill_chunk(cache, batch, qc, 32, kc, vc, scale, ob), reps)
+            qc = qd[:, s:s + cs].reshape(B * cs, HQ, D).contiguous()
+            kc = kd[:, s:s + cs].reshape(B * cs, HKV, D).contiguous()
+            vc = vd[:, s:s + cs].reshape(B * cs, HKV, D).contiguous()
+            t_tot += time_ms(lambda: swa.swa_prefill_chunk(cache, batch, qc, HQ, kc, vc, scale, ob), reps)
             w_tot += time_ms(lambda: swa.swa_cache_write(cache, batch, kc, vc), reps)
-        fl = 4.0 * 128 * 32 * B * band_pairs(0, N, W)
-        act = B * cs * (32 + 8 + 8 + 32) * 128 * 2  # q, k_new, v_new, out of one call
+        fl = 4.0 * D * HQ * B * band_pairs(0, N, W)
+        act = B * cs * (HQ + HKV + HKV + HQ) * D * 2  # q, k_new, v_new, out of one call
         sweep[f"C={cs}"] = {"prefill_ms": round(t_tot, 3), "prefill_tflops": round(fl / t_tot / 1e9, 1),
                             "cache_write_ms": round(w_tot, 3), "calls": N // cs,
                             "activation_mib_per_call": round(act / 2**20, 1)}
         del ob
-    res["chunk_sweep_4x32k_w4096"] = sweep
-    # the same chunk write with a cold Infinity Cache: 512 MiB written before each launch
     big = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     batch = swa.Batch([C] * B, [N - C] * B, list(range(B)))
-    kc = kd[:, N - C:].reshape(B * C, 8, 128).contiguous()
-    vc = vd[:, N - C:].reshape(B * C, 8, 128).contiguous()
+    kc = kd[:, N - C:].reshape(B * C, HKV, D).contiguous()
+    vc = vd[:, N - C:].reshape(B * C, HKV, D).contiguous()
     t_w_cold = time_ms_cold(lambda: swa.swa_cache_write(cache, batch, kc, vc), reps, lambda: big.fill_(1))
-    del big, kc, vc
-    del qd, kd, vd
+    del big, kc, vc, qd, kd, vd, cache
     tot_ms = sum(c[0] for c in chunks)
-    tot_fl = sum(c[2] for c in chunks)
-    wbytes = 2 * 2 * B * C * 8 * 128 * 2
-    res["chunked_4x32k_w4096"] = {
+    wbytes = 2 * 2 * B * C * HKV * D * 2
+    res = {"chunked_4x32k_w4096": {
         "prefill_ms_per_chunk": [round(c[0], 4) for c in chunks],
         "prefill_tflops_chunks_1_7": round(sum(c[2] for c in chunks[1:]) / sum(c[0] for c in chunks[1:]) / 1e9, 1),
-        "prefill_tflops_all": round(tot_fl / tot_ms / 1e9, 1),
+        "prefill_tflops_all": round(sum(c[2] for c in chunks) / tot_ms / 1e9, 1),
         "cache_write_ms_per_chunk": round(float(np.mean([c[1] for c in chunks])), 4),
         "cache_write_gbps": round(wbytes / float(np.mean([c[1] for c in chunks])) / 1e6, 1),
         "cache_write_cold_ms": round(t_w_cold, 4),
-        "cache_write_cold_gbps": round(wbytes / t_w_cold / 1e6, 1)}
-    del cache
+        "cache_write_cold_gbps": round(wbytes / t_w_cold / 1e6, 1)},
+        "chunk_sweep_4x32k_w4096": sweep}
+    if cpu:
+        leg = cpu_leg_chunked(q, k, v)
+        leg["gpu_tflops_chunks_1_7"] = res["chunked_4x32k_w4096"]["prefill_tflops_chunks_1_7"]
+        res["chunked_4x32k_w4096"]["cpu_oracle"] = leg
+    return res
 
-    # ragged mixed batch: 16 prefill + 32 decode sequences sharing one 48-row cache
+
+def suite_mixed(up, scale, reps, cpu: bool):
+    """Ragged mixed batch: 16 prefill + 32 decode sequences sharing one 48-row cache,
+    and the context-8192 variant.  Each launch is set against its roofline bound
+    (algorithmic FLOPs or bytes at the MFMA / HBM peak)."""
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    from sliding_window_gqa_swa_amd.workloads import ragged_mixed
+    dev = torch.device("cuda:0")
+    res = {}
     for variant in (False, True):
         wp, wd = ragged_mixed(1005, variant=variant)
-        cache = swa.Cache(torch.zeros((48, 8, W, 128), dtype=torch.bfloat16, device=dev),
-                          torch.zeros((48, 8, W, 128), dtype=torch.bfloat16, device=dev))
+        cache = bf16_cache(48, HKV, W, dev)
         for wl in (wp, wd):
-            hb = swa.Batch([s.start_pos - s.hist_lo for s in wl.seqs], [s.hist_lo for s in wl.seqs], wl.cache_idx)
-            swa.swa_cache_write(cache, hb, up(wl.hist_packed("k")), up(wl.hist_packed("v")))
+            write_history(cache, wl, up)
         pb = swa.Batch([s.n_new for s in wp.seqs], [s.start_pos for s in wp.seqs], wp.cache_idx)
         mq, mk, mv = up(wp.q), up(wp.k_new), up(wp.v_new)
-        mo = torch.empty((wp.total_tokens, 32, 128), dtype=torch.bfloat16, device=dev)
+        mo = torch.empty((wp.total_tokens, HQ, D), dtype=torch.bfloat16, device=dev)
         db = swa.Batch([1] * wd.num_seqs, [s.start_pos for s in wd.seqs], wd.cache_idx)
         dq, dk, dv = up(wd.q), up(wd.k_new), up(wd.v_new)
-        do = torch.empty((wd.num_seqs, 32, 128), dtype=torch.bfloat16, device=dev)
-        wsb = swa.swa_decode_workspace_size(cache, wd.num_seqs, 32)
+        do = torch.empty((wd.num_seqs, HQ, D), dtype=torch.bfloat16, device=dev)
+        wsb = swa.swa_decode_workspace_size(cache, wd.num_seqs, HQ)
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-        t_p = time_ms(lambda: swa.swa_prefill_chunk(cache, pb, mq, 32, mk, mv, scale, mo), reps)
+        t_p = time_ms(lambda: swa.swa_prefill_chunk(cache, pb, mq, HQ, mk, mv, scale, mo), reps)
         t_dw = time_ms(lambda: swa.swa_cache_write(cache, db, dk, dv), reps)
-        t_d = time_ms(lambda: swa.swa_decode(cache, db, dq, 32, scale, do, ws, wsb), reps)
-        pfl = 4.0 * 128 * 32 * sum(band_pairs(s.start_pos, s.n_new, W) for s in wp.seqs)
-        kvb = sum(2 * 8 * 128 * 2 * min(s.start_pos + 1, W) for s in wd.seqs)
-        # roofline bound of each launch: its algorithmic FLOPs or bytes at the
-        # MFMA / HBM peak, and the end-to-end time of the three launches
-        # against the sum of their bounds
-        wbytes = 2 * 2 * wd.num_seqs * 8 * 128 * 2
+        t_d = time_ms(lambda: swa.swa_decode(cache, db, dq, HQ, scale, do, ws, wsb), reps)
+        t_step = time_ms(lambda: swa.swa_decode_step(cache, db, dq, HQ, dk, dv, scale, do, ws, wsb), reps)
+        pfl = 4.0 * D * HQ * sum(band_pairs(s.start_pos, s.n_new, W) for s in wp.seqs)
+        kvb = sum(2 * HKV * D * 2 * min(s.start_pos + 1, W) for s in wd.seqs)
+        wbytes = 2 * 2 * wd.num_seqs * HKV * D * 2
         b_p, b_d, b_w = pfl / (PEAK_BF16_TFLOPS * 1e9), kvb / (PEAK_HBM_GBPS * 1e6), wbytes / (PEAK_HBM_GBPS * 1e6)
-        res["mixed_" + ("ctx8192" if variant else "loguniform")] = {
-            "prefill_ms": round(t_p, 4), "prefill_tflops": round(pfl / t_p / 1e9, 1),
-            "decode_us": round(t_d * 1e3, 1), "decode_gbps": round(kvb / t_d / 1e6, 1),
-            "decode_write_us": round(t_dw * 1e3, 1),
-            "bound_ms": {"prefill": round(b_p, 4), "decode": round(b_d, 4), "decode_write": round(b_w, 5)},
-            "end_to_end_ms": round(t_p + t_d + t_dw, 4),
-            "end_to_end_frac_of_bound": round((b_p + b_d + b_w) / (t_p + t_d + t_dw), 3)}
+        rec = {"prefill_ms": round(t_p, 4), "prefill_tflops": round(pfl / t_p / 1e9, 1),
+               "decode_us": round(t_d * 1e3, 1), "decode_gbps": round(kvb / t_d / 1e6, 1),
+               "decode_write_us": round(t_dw * 1e3, 1), "fused_decode_step_us": round(t_step * 1e3, 1),
+               "bound_ms": {"prefill": round(b_p, 4), "decode": round(b_d, 4), "decode_write": round(b_w, 5)},
+               "end_to_end_ms": round(t_p + t_d + t_dw, 4),
+               "end_to_end_frac_of_bound": round((b_p + b_d + b_w) / (t_p + t_d + t_dw), 3),
+               "end_to_end_fused_ms": round(t_p + t_step, 4),
+               "end_to_end_fused_frac_of_bound": round((b_p + b_d + b_w) / (t_p + t_step), 3)}
+        if cpu and not variant:
+            rec["cpu_oracle"] = cpu_leg_mixed(wp, wd)
+        res["mixed_" + ("ctx8192" if variant else "loguniform")] = rec
         del cache
     return res
+
+
+def suite_decode_g1(scale, reps, n_seqs=32):
+    """Decode at G = 1 (32 query heads over 32 KV heads: the VALU kernel), full
+    4096-slot rings, caches filled on the device from a seeded generator."""
+    import numpy as np
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(1006)
+    hkv = 32
+    cache = swa.Cache(torch.randn((n_seqs, hkv, W, D), generator=g, device=dev).to(torch.bfloat16),
+                      torch.randn((n_seqs, hkv, W, D), generator=g, device=dev).to(torch.bfloat16))
+    pos = np.random.default_rng(1006).integers(W, 8 * W, size=n_seqs)
+    db = swa.Batch([1] * n_seqs, [int(p) for p in pos], list(range(n_seqs)))
+    q = torch.randn((n_seqs, HQ, D), generator=g, device=dev).to(torch.bfloat16)
+    o = torch.empty((n_seqs, HQ, D), dtype=torch.bfloat16, device=dev)
+    wsb = swa.swa_decode_workspace_size(cache, n_seqs, HQ)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    t = time_ms(lambda: swa.swa_decode(cache, db, q, HQ, scale, o, ws, wsb), reps)
+    kvb = n_seqs * 2 * hkv * D * 2 * W
+    del cache
+    return {"decode_g1_32seq_w4096": {"us": round(t * 1e3, 1), "gbps": round(kvb / t / 1e6, 1),
+                                      "kv_bytes": kvb, "workspace_bytes": wsb}}
+
+
+def suite_multilayer_ring(up, reps):
+    """A 32-layer rolling cache for one 32768-token sequence: the rings of all layers are
+    one [32][1][8][4096][128] tensor; every layer writes its 8 chunks of 4096 tokens.
+    Device bytes are compared with a full 32K cache of the same layers (not allocated)."""
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    dev = torch.device("cuda:0")
+    L, N, C = 32, 32768, 4096
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated(dev)
+    kk = torch.empty((L, 1, HKV, W, D), dtype=torch.bfloat16, device=dev)
+    vv = torch.empty((L, 1, HKV, W, D), dtype=torch.bfloat16, device=dev)
+    ring_bytes = torch.cuda.memory_allocated(dev) - before
+    full_bytes = 2 * L * N * HKV * D * 2
+    caches = [swa.Cache(kk[layer], vv[layer]) for layer in range(L)]
+    g = torch.Generator(device=dev).manual_seed(1007)
+    kn = torch.randn((C, HKV, D), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((C, HKV, D), generator=g, device=dev).to(torch.bfloat16)
+    batches = [swa.Batch([C], [s], [0]) for s in range(0, N, C)]
+
+    def all_writes():
+        for c in caches:
+            for b in batches:
+                swa.swa_cache_write(c, b, kn, vn)
+
+    t = time_ms(all_writes, max(1, reps // 5))
+    del kk, vv, caches
+    return {"multilayer_ring_32x32k": {
+        "layers": L, "tokens": N, "ring_bytes": ring_bytes, "full_cache_bytes": full_bytes,
+        "full_over_ring": round(full_bytes / ring_bytes, 3),
+        "cache_writes_ms_all_layers_and_chunks": round(t, 3)}}
 
 
 def decode_step_latency(dcache, positions, rows, dq, dk, dv, scale, reps: int, steps_per_graph: int = 16):
@@ -270,16 +500,16 @@ def decode_step_latency(dcache, positions, rows, dq, dk, dv, scale, reps: int, s
     for n, short in ((1, False), (8, False), (64, False), (1, True), (8, True)):
         batch = swa.Batch([1] * n, [500] * n if short else positions[:n], rows[:n])
         q, k, v = dq[:n], dk[:n], dv[:n]
-        out = torch.empty((n, 32, 128), dtype=torch.bfloat16, device=dev)
-        nb = swa.swa_decode_workspace_size(dcache, n, 32)
+        out = torch.empty((n, HQ, D), dtype=torch.bfloat16, device=dev)
+        nb = swa.swa_decode_workspace_size(dcache, n, HQ)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
 
         def separate():
             swa.swa_cache_write(dcache, batch, k, v)
-            swa.swa_decode(dcache, batch, q, 32, scale, out, ws, nb)
+            swa.swa_decode(dcache, batch, q, HQ, scale, out, ws, nb)
 
         def fused():
-            swa.swa_decode_step(dcache, batch, q, 32, k, v, scale, out, ws, nb)
+            swa.swa_decode_step(dcache, batch, q, HQ, k, v, scale, out, ws, nb)
 
         rec = {}
         for name, fn in (("write_then_decode", separate), ("fused_step", fused)):
@@ -301,14 +531,17 @@ def decode_step_latency(dcache, positions, rows, dq, dk, dv, scale, reps: int, s
     return res
 
 
+# ----------------------------------------------------------------------------- main
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=16384)
-    ap.add_argument("--no-suite", action="store_true", help="skip the chunked / mixed / causal workloads")
+    ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only", choices=["chunked", "mixed", "decode_g1"],
+                    help="run one suite workload alone and print its record (for profilers)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -327,36 +560,39 @@ def main():
     swa.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    up = uploader(dev)
+    scale = 1.0 / D ** 0.5
 
-    def up(raw):
-        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).to(dev)
+    if args.only:
+        fn = {"chunked": lambda: suite_chunked(up, scale, 5, False),
+              "mixed": lambda: suite_mixed(up, scale, 5, False),
+              "decode_g1": lambda: suite_decode_g1(scale, 20)}[args.only]
+        print(json.dumps({"only": args.only, **fn()}))
+        return
 
     # ---- prefill workload (Mistral shape, 16K tokens, W = 4096)
-    W = 4096
     wp = mistral_prefill(1002, window=W, n=16384)
     n = wp.seqs[0].n_new
     pq, pk, pv = up(wp.q), up(wp.k_new), up(wp.v_new)
-    pout = torch.empty((n, 32, 128), dtype=torch.bfloat16, device=dev)
-    pcache = swa.Cache(torch.zeros((1, 8, W, 128), dtype=torch.bfloat16, device=dev),
-                       torch.zeros((1, 8, W, 128), dtype=torch.bfloat16, device=dev))
+    pout = torch.empty((n, HQ, D), dtype=torch.bfloat16, device=dev)
+    pcache = bf16_cache(1, HKV, W, dev)
     pbatch = swa.Batch([n], [0], [0])
-    band_flops = 4.0 * 128 * 32 * band_pairs(0, n, W)
-    pwrite_bytes = 2 * 2 * min(n, W) * 8 * 128 * 2
+    band_flops = 4.0 * D * HQ * band_pairs(0, n, W)
+    pwrite_bytes = 2 * 2 * min(n, W) * HKV * D * 2
 
     # ---- decode workload (64 sequences, full rings)
     wd = batched_decode(1004)
     B = wd.num_seqs
-    dcache = swa.Cache(torch.empty((B, 8, W, 128), dtype=torch.bfloat16, device=dev),
-                       torch.empty((B, 8, W, 128), dtype=torch.bfloat16, device=dev))
-    hb = swa.Batch([s.start_pos - s.hist_lo for s in wd.seqs], [s.hist_lo for s in wd.seqs], wd.cache_idx)
-    swa.swa_cache_write(dcache, hb, up(wd.hist_packed("k")), up(wd.hist_packed("v")))
+    dcache = swa.Cache(torch.empty((B, HKV, W, D), dtype=torch.bfloat16, device=dev),
+                       torch.empty((B, HKV, W, D), dtype=torch.bfloat16, device=dev))
+    write_history(dcache, wd, up)
     dbatch = swa.Batch([1] * B, [s.start_pos for s in wd.seqs], wd.cache_idx)
     dq, dk, dv = up(wd.q), up(wd.k_new), up(wd.v_new)
-    dout = torch.empty((B, 32, 128), dtype=torch.bfloat16, device=dev)
-    ws_bytes = swa.swa_decode_workspace_size(dcache, B, 32)
+    dout = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev)
+    ws_bytes = swa.swa_decode_workspace_size(dcache, B, HQ)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    kv_bytes = sum(2 * 8 * 128 * 2 * min(s.start_pos + 1, W) for s in wd.seqs)
-    dwrite_bytes = 2 * 2 * B * 8 * 128 * 2
+    kv_bytes = sum(2 * HKV * D * 2 * min(s.start_pos + 1, W) for s in wd.seqs)
+    dwrite_bytes = 2 * 2 * B * HKV * D * 2
     torch.cuda.synchronize()
 
     if args.calib_copy_mib:
@@ -369,13 +605,13 @@ def main():
 
     def step(ev):
         ev[0].record()
-        swa.swa_prefill_chunk(pcache, pbatch, pq, 32, pk, pv, wp.scale, pout)
+        swa.swa_prefill_chunk(pcache, pbatch, pq, HQ, pk, pv, wp.scale, pout)
         ev[1].record()
         swa.swa_cache_write(pcache, pbatch, pk, pv)
         ev[2].record()
         swa.swa_cache_write(dcache, dbatch, dk, dv)
         ev[3].record()
-        swa.swa_decode(dcache, dbatch, dq, 32, wd.scale, dout, ws, ws_bytes)
+        swa.swa_decode(dcache, dbatch, dq, HQ, wd.scale, dout, ws, ws_bytes)
         ev[4].record()
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -415,13 +651,15 @@ def main():
         "data": "synthetic: seeded N(0,1) activations rounded to bf16 (no weights, no dataset)",
         "config": {"workload": "mistral-shape SWA-GQA prefill 1x16384 W=4096 + chunk cache write "
                                "+ 64-sequence decode (W=4096 rings)",
-                   "global_batch": 1, "seq_len": n, "window": W, "n_q_heads": 32, "n_kv_heads": 8,
-                   "head_dim": 128, "decode_batch": B, "parallelism": "single GPU"},
+                   "global_batch": 1, "seq_len": n, "window": W, "n_q_heads": HQ, "n_kv_heads": HKV,
+                   "head_dim": D, "decode_batch": B, "parallelism": "single GPU"},
         "decode_kv_gbps": round(dec_gbps, 1),
         "parts_ms": {"prefill": round(t_pre, 4), "cache_write_chunk": round(t_pw, 4),
                      "cache_write_decode": round(t_dw, 4), "decode": round(t_dec, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": pmc_source() if traffic is not None else
+                     "null: the prefill source changed since the committed counters were taken",
                      "kernel": PREFILL_KERNEL, "algorithmic_flops_per_launch": band_flops},
         "sclk": sclk,
         "decode_roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
@@ -432,15 +670,22 @@ def main():
         "pages_context": {"swa_vs_standard_speedup_at_16k_w4096": 2.0, "cache_memory_reduction_at_32k": 8.0,
                           "hardware": "not stated"},
     }
+    cpu = not args.no_cpu_baseline
     if not args.no_suite:
-        result["suite"] = suite(up, pq, pk, pv, pout, wp.scale, reps=10)
-        result["suite"]["decode_step_latency"] = decode_step_latency(
-            dcache, [s.start_pos for s in wd.seqs], list(wd.cache_idx), dq, dk, dv, wd.scale, reps=50)
-        result["suite"]["swa_vs_causal_speedup_16k"] = round(
-            result["suite"]["causal_prefill_16k"]["ms"] / t_pre, 3)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wp, args.cpu_sample_rows)
+        s = suite_causal_and_no_skip(pq, pk, pv, pout, wp.scale, t_pre, reps=10)
+        s.update(suite_chunked(up, scale, 10, cpu))
+        s.update(suite_mixed(up, scale, 10, cpu))
+        s.update(suite_decode_g1(scale, 20))
+        s["decode_step_latency"] = decode_step_latency(
+            dcache, [x.start_pos for x in wd.seqs], list(wd.cache_idx), dq, dk, dv, wd.scale, reps=50)
+        del dcache, pcache
+        s.update(suite_multilayer_ring(up, 10))
+        result["suite"] = s
+    if cpu:
+        result["cpu_baseline"] = cpu_baseline_prefill(wp)
         result["cpu_baseline"]["gpu_over_cpu"] = round(tflops / result["cpu_baseline"]["value"], 1)
+        result["cpu_baseline_other_configs"] = {"tiny_fp32": cpu_leg_tiny(), "decode_64seq": cpu_leg_decode(wd)}
+        result["cpu_baseline_other_configs"]["decode_64seq"]["gpu_kv_gbps"] = round(dec_gbps, 1)
     print(json.dumps(result))
 
 
