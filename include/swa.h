@@ -174,14 +174,21 @@ int swa_prefill_chunk_no_tile_skip(const swa_cache *cache, const swa_batch *batc
 /*
  * Bytes of device workspace swa_decode and swa_decode_step need for this cache
  * shape, batch size and head count (0 when the plan needs none).  Returns 0 for
- * invalid input.  The plan may split each sequence's window into S parts that
- * separate workgroups attend to; the workspace then holds one partial result
- * of head_dim + 2 floats per (sequence, query head, part), i.e.
- * num_seqs * n_q_heads * S * (head_dim + 2) * 4 bytes, and a merge launch
- * combines them.  Guarantees: S depends only on the arguments of this call;
- * 1 <= S <= max(1, window / 128); S = 1 (no workspace) when num_seqs *
- * n_kv_heads >= 2048 or for SWA_DTYPE_F32; and the total never exceeds
- * SWA_DECODE_WORKSPACE_MAX_BYTES.
+ * invalid input.  When one workgroup per (sequence, KV head) would leave the
+ * GPU short of work, the plan spreads the attention over more workgroups; the
+ * workspace holds their partial results (head_dim + 2 floats per query head)
+ * and a merge launch combines them.  Two plans:
+ *   - split: each window in S parts, one partial per (sequence, query head,
+ *     part): num_seqs * n_q_heads * S * (head_dim + 2) * 4 bytes,
+ *     2 <= S <= window / 256;
+ *   - stream (bf16 on the matrix-core kernel -- G >= 2, or head_dim < 128 --
+ *     with at most 64 sequences): the valid slots of the whole batch in equal
+ *     ranges, one per workgroup, which leaves at most two partials of the G
+ *     query heads of a KV head: N * 2 * G * (head_dim + 2) * 4 bytes for
+ *     N <= 512 workgroups.
+ * Guarantees: the size depends only on the arguments of this call; it is 0 for
+ * SWA_DTYPE_F32, for window < 512 and when num_seqs * n_kv_heads >= 2048; it
+ * never exceeds SWA_DECODE_WORKSPACE_MAX_BYTES.
  */
 #define SWA_DECODE_WORKSPACE_MAX_BYTES ((size_t)8 << 20)
 size_t swa_decode_workspace_size(const swa_cache *cache, int32_t num_seqs, int32_t n_q_heads);

@@ -128,7 +128,7 @@ static bool decode_on_valu(int32_t group, int32_t head_dim) { return group == 1 
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, int32_t head_dim, int32_t window,
                        int32_t dtype) {
-  DecodePlan pl{1, window, 0};
+  DecodePlan pl{1, window, 0, 0, 0};
   if (dtype != SWA_DTYPE_BF16 || num_seqs <= 0) return pl;
   // Workgroups per launch to aim for.  The VALU kernel (G = 1) wants >= ~2048
   // (8 per CU).  The matrix-core kernel (G >= 2) holds 2 workgroups per CU, so
@@ -136,15 +136,30 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   // ring and need no merge launch.  A split keeps >= 256 slots either way, so
   // that each wave streams several 16 KiB steps.
   const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
-  const int64_t target_wg = decode_on_valu(n_q_heads / n_kv_heads, head_dim) ? 2048 : 512;
+  const int32_t group = n_q_heads / n_kv_heads;
+  const bool valu = decode_on_valu(group, head_dim);
+  const int64_t target_wg = valu ? 2048 : 512;
   int64_t max_splits = std::max<int64_t>(1, window / 256);
   int64_t splits = std::min<int64_t>(max_splits, std::max<int64_t>(1, (target_wg + pairs - 1) / pairs));
   int64_t len = (window + splits - 1) / splits;
   len = (len + 31) / 32 * 32;
   splits = (window + len - 1) / len;
+  if (splits == 1) return pl;
+  if (!valu && num_seqs <= kStreamMaxSeqs && window <= (1 << 21)) {
+    // Too few rings to fill the chip one workgroup each: the matrix-core
+    // kernel runs in stream mode, where every workgroup takes an equal share
+    // of the batch's valid slots whatever each sequence's context length,
+    // with at most two partial results per workgroup.
+    const int64_t wg = std::min<int64_t>(target_wg, (pairs * window + kStreamMinRows - 1) / kStreamMinRows);
+    pl.stream_wg = (int32_t)wg;
+    pl.acc_floats = (size_t)wg * 2 * group * head_dim;
+    pl.workspace_bytes = (size_t)wg * 2 * group * (head_dim + 2) * sizeof(float);
+    return pl;
+  }
   pl.splits = (int32_t)splits;
   pl.split_len = (int32_t)len;
-  if (splits > 1) pl.workspace_bytes = (size_t)num_seqs * n_q_heads * splits * (head_dim + 2) * sizeof(float);
+  pl.acc_floats = (size_t)num_seqs * n_q_heads * splits * head_dim;
+  pl.workspace_bytes = (size_t)num_seqs * n_q_heads * splits * (head_dim + 2) * sizeof(float);
   return pl;
 }
 
@@ -183,11 +198,12 @@ static int decode_impl(const swa_cache *cache, const swa_batch *batch, const voi
   p.n_q_heads = n_q_heads;
   p.splits = pl.splits;
   p.split_len = pl.split_len;
+  p.stream_wg = pl.stream_wg;
   p.sm_scale = sm_scale;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   if (pl.workspace_bytes > 0) {
     p.ws_acc = (float *)workspace;
-    p.ws_ml = p.ws_acc + (size_t)batch->num_seqs * n_q_heads * pl.splits * cache->head_dim;
+    p.ws_ml = p.ws_acc + pl.acc_floats;
   }
   hipError_t e;
   const int group = n_q_heads / cache->n_kv_heads;

@@ -28,10 +28,10 @@ template <int D>
 __global__ __launch_bounds__(64 * kWaves) void attend_f32_kernel(PrefillParams p, int mode) {
   const bool decode = mode != 0;
   __shared__ float sq[kWaves][D];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.y;
-  const int t = blockIdx.x;
-  const int h = blockIdx.z * kWaves + wave;
+  const int lane = thread_x() & 63, wave = thread_x() >> 6;
+  const int b = wg_y();
+  const int t = wg_x();
+  const int h = wg_z() * kWaves + wave;
   const int hq = p.n_q_heads;
   const int hkv = p.cache.n_kv_heads;
   const int G = hq / hkv;

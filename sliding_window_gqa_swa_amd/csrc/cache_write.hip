@@ -16,8 +16,8 @@
 namespace swa {
 
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
-  const int b = blockIdx.y;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = wg_y();
+  const int64_t idx = (int64_t)wg_x() * 256 + thread_x();
   const int per_token = p.n_kv_heads * p.row_chunks;
   const int64_t tw = idx / per_token;  // index among the tokens this sequence writes
   const int rem = (int)(idx - tw * per_token);

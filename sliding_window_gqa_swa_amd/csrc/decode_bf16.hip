@@ -53,12 +53,12 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
   __shared__ float sm_m[kRowWaves][G];
   __shared__ float sm_l[kRowWaves][G];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_x(), lane = tid & 63, wave = tid >> 6;
   const int hg = wave % NHG, rw = wave / NHG;
   const int grp = lane >> 3, c = lane & 7;
   const int splits = p.splits;
-  const int sp = blockIdx.x % splits;
-  const int bg = blockIdx.x / splits;
+  const int sp = wg_x() % splits;
+  const int bg = wg_x() / splits;
   const int hkv = p.cache.n_kv_heads;
   const int g = bg % hkv, b = bg / hkv;
   const int W = p.cache.window;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
 // One thread per output element: blockDim = head_dim.
 __global__ __launch_bounds__(kD) void decode_combine_bf16_kernel(DecodeParams p) {
   constexpr int kBatch = 8;
-  const int bh = blockIdx.x, d = threadIdx.x;
+  const int bh = wg_x(), d = thread_x();
   const int D = p.cache.head_dim;
   const int S = p.splits;
   const float *ml = p.ws_ml + (size_t)bh * S * 2;

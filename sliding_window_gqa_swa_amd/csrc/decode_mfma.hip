@@ -11,8 +11,14 @@
 // With G query heads per KV head the per-row work is a small matrix product,
 // so it runs on v_mfma_f32_16x16x32_bf16 (the G heads padded to 16 columns)
 // instead of per-head VALU dot products, which cost more per byte as G grows:
-//   * One workgroup = (sequence, KV head, split of the window), 4 waves; a
-//     wave takes 32-key steps r0 = split start + 32 w + 128 j.
+//   * Split mode: one workgroup = (sequence, KV head, split of the window),
+//     4 waves; a wave takes 32-key steps r0 = split start + 32 w + 128 j.
+//   * Stream mode (batches too small to fill the chip with whole windows):
+//     the valid slots of all (sequence, KV head) pairs are laid end to end and
+//     cut into equal ranges, one per workgroup, which attends to its range one
+//     pair piece at a time, so that short and long contexts in one batch cost
+//     the same per slot.  Pieces that are parts of pairs leave partial results
+//     (at most two per workgroup) for a merge launch.
 //   * S^T (keys x heads) = K Q^T: the K rows are loaded from HBM straight into
 //     the MFMA A-operand layout (lane -> row lane % 16, 8 consecutive d);
 //     Q^T is the B operand, loaded once.
@@ -28,8 +34,9 @@
 //     does not wait for the prefetch before reading.
 //   * Keys past the split (a partial last step) read the split's last valid
 //     row and are masked to -inf: unwritten slots are never read.
-//   * Waves merge through LDS (log-sum-exp), splits through the workspace and
-//     the combine kernel of decode_bf16.hip.
+//   * Waves merge through LDS (log-sum-exp); splits through the workspace and
+//     the combine kernel of decode_bf16.hip, stream pieces through the
+//     workspace and the stream combine kernel below.
 #include "device_common.h"
 #include "swa_internal.h"
 
@@ -82,34 +89,38 @@ struct RowGeo {
   }
 };
 
+template <int D>
+using VBuf = unsigned char[kWaves][RowGeo<D>::kVBufB];
+
+// Where the result of one attended range goes: the final bf16 rows of out
+// (acc == nullptr), or partial results -- unnormalised output sums, running
+// max in log2 units and weight sum -- of query head hh of the group at
+// acc[(base + hh * stride) * D] and ml[(base + hh * stride) * 2].
+struct RangeOut {
+  float *acc;
+  float *ml;
+  size_t base;
+  int stride;
+};
+
+// The G query heads of KV head g of sequence b (at position pos, cache row
+// crow) attend to ring slots [r_begin, r_end), by the whole workgroup.  On
+// return each wave is past its own LDS reads, but vbuf_a, which held the wave
+// merge, may still be read by the others: a barrier comes before it is refilled.
 template <int G, int D>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+__device__ __forceinline__ void attend_range(const DecodeParams &p, VBuf<D> &vbuf_a, VBuf<D> &vbuf_b, int b, int g,
+                                             int pos, int crow, int r_begin, int r_end, RangeOut dst) {
   using Rg = RowGeo<D>;
   constexpr int kD = D, kRowB = Rg::kRowB, kVBufB = Rg::kVBufB, kC = Rg::kC, kRpl = Rg::kRpl;
   constexpr int kKS = Rg::kKS, kDB = Rg::kDB;
-  // two V buffers per wave, as two objects; after the loop vbuf_a holds the merge
-  __shared__ __attribute__((aligned(16))) unsigned char vbuf_a[kWaves][kVBufB];
-  __shared__ __attribute__((aligned(16))) unsigned char vbuf_b[kWaves][kVBufB];
   static_assert(kWaves * G * (kD + 2) * 4 <= kWaves * kVBufB, "the wave merge fits in vbuf_a");
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = thread_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, lg = lane >> 4;  // MFMA column (query head) and lane group
-  const int splits = p.splits;
-  const int sp = blockIdx.x % splits;
-  const int bg = blockIdx.x / splits;
   const int hkv = p.cache.n_kv_heads;
-  const int g = bg % hkv, b = bg / hkv;
   const int W = p.cache.window;
   const int hq = p.n_q_heads;
-
-  const int pos = __builtin_amdgcn_readfirstlane(p.seq.start_pos[b]);
-  const int n_valid = min(pos + 1, W);
-  const int crow = p.seq.cache_idx ? __builtin_amdgcn_readfirstlane(p.seq.cache_idx[b]) : b;
-  // uniform by construction; readfirstlane lets the compiler branch on them with scalar branches
-  const int len = __builtin_amdgcn_readfirstlane(seq_split_len(n_valid, splits, p.split_len));
-  const int r_begin = __builtin_amdgcn_readfirstlane(sp * len);
-  const int r_end = __builtin_amdgcn_readfirstlane(min(r_begin + len, n_valid));
   const float c = p.scale_log2;
 
   const size_t ring0 = ((size_t)crow * hkv + g) * (size_t)W * kD;
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const uint16_t *vring = (const uint16_t *)p.cache.v + ring0;
 
   // fused step: the new token's row comes from k_new / v_new and is written to
-  // its slot by the workgroup whose split holds it (nobody else reads the slot)
+  // its slot by the workgroup whose range holds it (nobody else reads the slot)
   const bool fused = p.k_new != nullptr;
   const int new_slot = fused ? pos % W : -1;
   const uint16_t *knew = fused ? (const uint16_t *)p.k_new + ((size_t)b * hkv + g) * kD : nullptr;
@@ -126,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // kC lanes copy the K row, kC lanes the V row, 16 bytes each
     const int ch = lane % kC;
     const uint16_t *src = lane < kC ? knew : vnew;
-    uint16_t *dst = (uint16_t *)(lane < kC ? p.cache_k_out : p.cache_v_out) + ring0 + (size_t)new_slot * kD;
-    *(u32x4 *)(dst + 8 * ch) = *(const u32x4 *)(src + 8 * ch);
+    uint16_t *row = (uint16_t *)(lane < kC ? p.cache_k_out : p.cache_v_out) + ring0 + (size_t)new_slot * kD;
+    *(u32x4 *)(row + 8 * ch) = *(const u32x4 *)(src + 8 * ch);
   }
 
   bf16x8 qf[kKS];  // Q^T as the B operand, loaded after the first K/V loads are issued
@@ -310,24 +321,165 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         os += sm_acc[(w * G + hh) * kD + d] * f;
       }
     }
-    const int h = g * G + hh;
-    if (splits == 1) {
-      ((uint16_t *)p.out)[((size_t)b * hq + h) * kD + d] = (uint16_t)pack_bf16(os / ls, 0.f);
+    if (dst.acc == nullptr) {
+      ((uint16_t *)p.out)[((size_t)b * hq + g * G + hh) * kD + d] = (uint16_t)pack_bf16(os / ls, 0.f);
     } else {
-      const size_t slot = ((size_t)b * hq + h) * splits + sp;
-      p.ws_acc[slot * kD + d] = os;
+      const size_t slot = dst.base + (size_t)hh * dst.stride;
+      dst.acc[slot * kD + d] = os;
       if (d == 0) {
-        p.ws_ml[slot * 2] = mx;
-        p.ws_ml[slot * 2 + 1] = ls;
+        dst.ml[slot * 2] = mx;
+        dst.ml[slot * 2 + 1] = ls;
       }
     }
   }
 }
 
+template <int G, int D, bool kStream>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  // two V buffers per wave, as two objects; after a range vbuf_a holds the merge
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf_a[kWaves][RowGeo<D>::kVBufB];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf_b[kWaves][RowGeo<D>::kVBufB];
+  const int hkv = p.cache.n_kv_heads;
+  const int W = p.cache.window;
+  if constexpr (!kStream) {
+    // split mode: one workgroup = (sequence, KV head, split of the window)
+    const int splits = p.splits;
+    const int sp = wg_x() % splits;
+    const int bg = wg_x() / splits;
+    const int g = bg % hkv, b = bg / hkv;
+    const int pos = __builtin_amdgcn_readfirstlane(p.seq.start_pos[b]);
+    const int crow = p.seq.cache_idx ? __builtin_amdgcn_readfirstlane(p.seq.cache_idx[b]) : b;
+    const int n_valid = min(pos + 1, W);
+    // uniform by construction; readfirstlane lets the compiler branch on them with scalar branches
+    const int len = __builtin_amdgcn_readfirstlane(seq_split_len(n_valid, splits, p.split_len));
+    const int r_begin = __builtin_amdgcn_readfirstlane(sp * len);
+    const int r_end = __builtin_amdgcn_readfirstlane(min(r_begin + len, n_valid));
+    RangeOut dst{nullptr, nullptr, 0, 0};
+    if (splits > 1) dst = RangeOut{p.ws_acc, p.ws_ml, ((size_t)b * p.n_q_heads + g * G) * splits + sp, splits};
+    attend_range<G, D>(p, vbuf_a, vbuf_b, b, g, pos, crow, r_begin, r_end, dst);
+  } else {
+    // stream mode: the valid slots of the pairs (b, g), laid end to end
+    // sequence-major -- pair (b, g) holds rows hkv S(b) + g nv(b) .. + nv(b) - 1,
+    // with nv(b) its valid slots and S(b) those of the sequences before b --
+    // are cut into ranges of L rows; this workgroup attends to range wg_x(),
+    // piece by piece (one piece per pair it meets).  A piece that is a whole
+    // pair gives final rows; the first and the last piece may be parts of pairs
+    // and go to the workgroup's partial slots 0 and 1.  Every wave computes
+    // the same plan from the batch (at most 64 sequences, one per lane).
+    const int lane = thread_x() & 63;
+    const int ns = p.seq.num_seqs;
+    const int pos_l = lane < ns ? p.seq.start_pos[lane] : 0;
+    const int crow_l = lane < ns ? (p.seq.cache_idx ? p.seq.cache_idx[lane] : lane) : 0;
+    const int nv_l = lane < ns ? max(0, min(pos_l + 1, W)) : 0;
+    int incl = nv_l;  // inclusive prefix sum over the sequences
+#pragma unroll
+    for (int dl = 1; dl < 64; dl <<= 1) {
+      const int t = __shfl_up(incl, dl);
+      if (lane >= dl) incl += t;
+    }
+    const int total = hkv * __builtin_amdgcn_readlane(incl, 63);
+    const int L = stream_range_rows(total, p.stream_wg);
+    const int R0 = wg_x() * L;
+    if (R0 >= total) return;
+    const int R1 = min(R0 + L, total);
+    // the first sequence whose pairs reach past R0 (lanes past the batch hold
+    // the total, so a lane below ns is found first)
+    int b = __builtin_ffsll((long long)__builtin_amdgcn_ballot_w64(hkv * incl > R0)) - 1;
+    int nvb = __builtin_amdgcn_readlane(nv_l, b);
+    const int off = R0 - hkv * (__builtin_amdgcn_readlane(incl, b) - nvb);  // 0 <= off < hkv nvb
+    int g = off / nvb;
+    int r_begin = off - g * nvb;
+    int cur = R0;
+    for (;;) {
+      const int r_end = min(nvb, r_begin + (R1 - cur));
+      RangeOut dst{nullptr, nullptr, 0, 0};
+      if (r_begin > 0 || r_end < nvb)
+        dst = RangeOut{p.ws_acc, p.ws_ml, ((size_t)wg_x() * 2 + (cur == R0 ? 0 : 1)) * G, 1};
+      attend_range<G, D>(p, vbuf_a, vbuf_b, b, g, __builtin_amdgcn_readlane(pos_l, b),
+                         __builtin_amdgcn_readlane(crow_l, b), r_begin, r_end, dst);
+      cur += r_end - r_begin;
+      if (cur >= R1) break;
+      r_begin = 0;
+      if (++g == hkv) {
+        g = 0;
+        if (++b >= ns) break;
+        nvb = __builtin_amdgcn_readlane(nv_l, b);
+      }
+      __syncthreads();  // vbuf_a held the wave merge
+    }
+  }
+}
+
+// Stream mode: merge the partial results of each (sequence, query head) whose
+// pair of slots spans several workgroups' ranges; pairs inside one range
+// already have their rows.  Each wave recomputes the decode kernel's plan from
+// the batch (lane i holds sequence i).  The partials come from workgroups
+// w0 .. w1 (slot 1 of w0 when the pair starts inside w0's range, else slot 0).
+// One thread per output element; 64 ceil(D / 64) threads, so that every wave
+// is whole for the sums over the batch.
+__global__ __launch_bounds__(128) void decode_combine_stream_kernel(DecodeParams p) {
+  const int bh = wg_x(), d = thread_x(), lane = d & 63;
+  const int D = p.cache.head_dim, W = p.cache.window;
+  const int hq = p.n_q_heads, hkv = p.cache.n_kv_heads, G = hq / hkv;
+  const int b = bh / hq, h = bh % hq, g = h / G, hh = h % G;
+  const int ns = p.seq.num_seqs;
+  const int nv = lane < ns ? max(0, min(p.seq.start_pos[lane] + 1, W)) : 0;
+  const int total = hkv * __builtin_amdgcn_readfirstlane(wave_sum_i32(nv));
+  const int before = __builtin_amdgcn_readfirstlane(wave_sum_i32(lane < b ? nv : 0));
+  const int nvb = __builtin_amdgcn_readlane(nv, b);
+  if (nvb == 0 || d >= D) return;
+  const int L = stream_range_rows(total, p.stream_wg);
+  const int P = hkv * before + g * nvb;
+  const int w0 = P / L, w1 = (P + nvb - 1) / L;
+  if (w0 == w1) return;
+  const int s0 = P == w0 * L ? 0 : 1;
+  // kBatch partials per round, loaded together (indexes clamped to w1, the
+  // extra values masked), merged into the running max and sums
+  constexpr int kBatch = 8;
+  float mx = -INFINITY, ls = 0.f, os = 0.f;
+  for (int wb = w0; wb <= w1; wb += kBatch) {
+    float mv[kBatch], lv[kBatch], av[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) {
+      const int w = min(wb + i, w1);
+      const size_t slot = ((size_t)w * 2 + (w == w0 ? s0 : 0)) * G + hh;
+      const float m_ld = p.ws_ml[slot * 2];
+      mv[i] = wb + i <= w1 ? m_ld : -INFINITY;
+      lv[i] = p.ws_ml[slot * 2 + 1];
+      av[i] = p.ws_acc[slot * D + d];
+    }
+    float bm = mx;
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) bm = fmaxf(bm, mv[i]);
+    if (bm == -INFINITY) continue;
+    const float r = exp2f(mx - bm);  // 0 while nothing is merged yet
+    ls *= r;
+    os *= r;
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) {
+      if (mv[i] == -INFINITY) continue;  // past w1, or a partial without keys
+      const float f = exp2f(mv[i] - bm);
+      ls += lv[i] * f;
+      os += av[i] * f;
+    }
+    mx = bm;
+  }
+  ((uint16_t *)p.out)[(size_t)bh * D + d] = (uint16_t)pack_bf16(os / ls, 0.f);
+}
+
 template <int G, int D>
 hipError_t launch_gd(const DecodeParams &p, hipStream_t stream) {
+  if (p.stream_wg > 0) {
+    if (p.seq.num_seqs > kStreamMaxSeqs) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, true>), dim3((unsigned)p.stream_wg), dim3(kThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_combine_stream_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads),
+                       dim3((unsigned)(64 * ((D + 63) / 64))), 0, stream, p);
+    return hipGetLastError();
+  }
   const unsigned n_wg = (unsigned)p.seq.num_seqs * p.cache.n_kv_heads * p.splits;
-  hipLaunchKernelGGL((decode_mfma_kernel<G, D>), dim3(n_wg), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, D, false>), dim3(n_wg), dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine_bf16(p, stream);

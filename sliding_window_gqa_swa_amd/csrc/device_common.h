@@ -17,6 +17,16 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Workgroup and work-item indices read straight from the hardware registers.
+// Under this library's float flags (no IEEE mode) the blockIdx / threadIdx
+// accessors stay calls into the device library, which is built with IEEE mode
+// on and so cannot be inlined; a call also hides that the workgroup index is
+// uniform, and loops bounded by it would branch per lane.
+__device__ __forceinline__ int wg_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int wg_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ int wg_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+__device__ __forceinline__ int thread_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 
 // bf16 bit patterns packed two per 32-bit word: low half is the first element.
@@ -83,6 +93,13 @@ __device__ __forceinline__ float max_over_groups8(float x) {
 __device__ __forceinline__ float sum_over_groups8(float x) {
   x += dpp_f<kDppRowRor8>(x);
   return add_pair32(add_pair16(x));
+}
+
+// Sum of an int over the 64 lanes of a wave (every lane must be active).
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
 }
 
 // Workgroups are dispatched to the XCDs round-robin (id mod 8).  Give each XCD

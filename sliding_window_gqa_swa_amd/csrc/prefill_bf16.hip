@@ -113,14 +113,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   constexpr int kBQ = 32 * kWph;    // query positions per workgroup
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = thread_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave choices scalar
   // Work order (KV head, sequence, query tile from the last), dealt to the XCDs
   // in contiguous ranges: with 8 KV heads every XCD takes one head of every
   // sequence -- the same share of a ragged batch -- and only that head's K/V
   // passes through its L2; the workgroups resident on an XCD at a time work on
   // neighbouring query tiles of one sequence, whose windows overlap.
-  const int work = __builtin_amdgcn_readfirstlane(xcd_logical_id(blockIdx.x, p.n_work));
+  const int work = __builtin_amdgcn_readfirstlane(xcd_logical_id(wg_x(), p.n_work));
   const int tps = p.tiles_per_seq;
   const int nseq = p.seq.num_seqs;
   const int hkv = p.cache.n_kv_heads;

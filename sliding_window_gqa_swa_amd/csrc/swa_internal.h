@@ -66,11 +66,15 @@ struct DecodeParams {
   const void *v_new;
   void *cache_k_out;
   void *cache_v_out;
-  float *ws_acc;  // [num_seqs][n_q_heads][splits][head_dim]
-  float *ws_ml;   // [num_seqs][n_q_heads][splits][2]  (max in log2 units, sum)
+  // Partial results: split mode [num_seqs][n_q_heads][splits][head_dim] and
+  // [..][2] (max in log2 units, sum); stream mode [stream_wg][2][G][head_dim]
+  // and [..][2], two slots per workgroup.
+  float *ws_acc;
+  float *ws_ml;
   int32_t n_q_heads;
   int32_t splits;
   int32_t split_len;  // slots per split for a full window (see seq_split_len)
+  int32_t stream_wg;  // > 0: stream mode with this many workgroups (see stream_range_rows)
   float scale_log2;
   float sm_scale;
 };
@@ -88,10 +92,27 @@ __device__ __forceinline__ int seq_split_len(int n_valid, int splits, int plan_l
   return len < plan_len ? len : plan_len;
 }
 
-// Decode plan: how the window of each (sequence, KV head) is split across workgroups.
+// Stream mode of the matrix-core decode (small batches): the valid slots of
+// all (sequence, KV head) pairs, laid end to end sequence-major, are cut into
+// stream_wg contiguous ranges of equal length, one per workgroup, so that
+// sequences of different context lengths cost the same per slot.  The range
+// length is a multiple of 32, at least kStreamMinRows; total_rows <= 2^30.
+constexpr int kStreamMinRows = 256;
+constexpr int kStreamMaxSeqs = 64;  // one wave scans the batch
+__host__ __device__ __forceinline__ int stream_range_rows(int total_rows, int stream_wg) {
+  int len = (total_rows + stream_wg - 1) / stream_wg;
+  len = (len + 31) & ~31;
+  return len > kStreamMinRows ? len : kStreamMinRows;
+}
+
+// Decode plan: how the window of each (sequence, KV head) is split across
+// workgroups (split mode), or how many workgroups share the batch's slots
+// (stream mode, stream_wg > 0).
 struct DecodePlan {
   int32_t splits;
   int32_t split_len;
+  int32_t stream_wg;
+  size_t acc_floats;  // floats of ws_acc; ws_ml follows them
   size_t workspace_bytes;
 };
 DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, int32_t head_dim,

@@ -217,41 +217,57 @@ def test_decode_step_noalloc_argument_checks():
 
 def test_workspace_plan():
     c = cache(window=4096, n_cache=64)
-    # 64 sequences x 8 KV heads (G = 4): 512 workgroups fill the chip, one split per ring
+    # 64 sequences x 8 KV heads (G = 4): 512 workgroups fill the chip, one per ring
     assert swa.swa_decode_workspace_size(c, 64, 32) == 0
-    # 8 sequences: the window is split; workspace = B x Hq x splits x (D + 2) floats
-    sz = swa.swa_decode_workspace_size(c, 8, 32)
-    assert sz > 0 and sz % (8 * 32 * (128 + 2) * 4) == 0
-    # G = 1 (32 KV heads) aims at more workgroups: 16 sequences already split
+    # 8 sequences (G = 4): stream mode, 512 workgroups x 2 partials x 4 heads x (D + 2) floats
+    assert swa.swa_decode_workspace_size(c, 8, 32) == 512 * 2 * 4 * (128 + 2) * 4
+    # one sequence, one KV head, G = 2: 4096 slots give 16 ranges of 256
+    c1 = cache(window=4096, n_cache=1, n_kv_heads=1)
+    assert swa.swa_decode_workspace_size(c1, 1, 2) == 16 * 2 * 2 * (128 + 2) * 4
+    # 65 sequences x 4 KV heads (G = 8): past the stream batch limit, split plan
+    c8 = cache(window=4096, n_cache=65, n_kv_heads=4)
+    sz8 = swa.swa_decode_workspace_size(c8, 65, 32)
+    assert sz8 > 0 and sz8 % (65 * 32 * (128 + 2) * 4) == 0
+    # G = 1 at head_dim 128 (VALU kernel) aims at more workgroups: 16 sequences already split
     sz1 = swa.swa_decode_workspace_size(cache(window=4096, n_cache=64, n_kv_heads=32), 16, 32)
     assert sz1 > 0 and sz1 % (16 * 32 * (128 + 2) * 4) == 0
     assert swa.swa_decode_workspace_size(c, 0, 32) == 0
     assert swa.swa_decode_workspace_size(cache(window=64), 2, 32) == 0      # too short to split
+    assert swa.swa_decode_workspace_size(cache(window=511), 2, 32) == 0
     assert swa.swa_decode_workspace_size(cache(dtype=swa.SWA_DTYPE_F32), 2, 32) == 0
     assert swa.swa_decode_workspace_size(cache(window=0), 2, 32) == 0       # invalid -> 0
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("window", [1, 127, 128, 255, 256, 1000, 4096, 4097, 32768, 2**20])
-@pytest.mark.parametrize("head_dim", [128])
+@pytest.mark.parametrize("window", [1, 127, 128, 255, 256, 511, 512, 1000, 4096, 4097, 32768, 2**20, 2**22])
+@pytest.mark.parametrize("head_dim", [128, 64, 16])
 def test_workspace_size_guarantees(group, window, head_dim):
     """The guarantees stated with swa_decode_workspace_size: the size is a whole
-    number S of per-part partial results (head_dim + 2 floats per sequence and
-    query head), 1 <= S <= max(1, W / 128), no workspace once the batch alone
-    gives 2048 (sequence, KV head) pairs, and never more than the stated maximum."""
+    number of partial results of head_dim + 2 floats, laid out by one of the two
+    plans -- split (num_seqs x n_q_heads x S, 2 <= S <= W / 256) or stream (at
+    most 64 sequences, matrix-core kernel: N x 2 x G with N <= 512) -- none for
+    W < 512 or once the batch alone gives 2048 (sequence, KV head) pairs, and
+    never more than the stated maximum."""
     hkv = 32 // group
+    on_valu = group == 1 and head_dim == 128
     c = cache(window=window, n_cache=65535, n_kv_heads=hkv, head_dim=head_dim)
     max_bytes = int(re.search(r"#define SWA_DECODE_WORKSPACE_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)",
                               open(HEADER).read()).group(1)) << 20
     for b in list(range(1, 70)) + [127, 128, 129, 255, 256, 511, 512, 513, 4095, 4096, 65535]:
         sz = swa.swa_decode_workspace_size(c, b, 32)
-        per_part = b * 32 * (head_dim + 2) * 4
-        assert sz % per_part == 0, (b, sz)
-        parts = max(1, sz // per_part)
-        assert 1 <= parts <= max(1, window // 128), (b, parts)
-        if b * hkv >= 2048:
-            assert sz == 0, b
         assert sz <= max_bytes, (b, sz)
+        if window < 512 or b * hkv >= 2048:
+            assert sz == 0, b
+        if sz == 0:
+            continue
+        part = (head_dim + 2) * 4
+        assert sz % part == 0, (b, sz)
+        parts = sz // part
+        if not on_valu and b <= 64:
+            assert parts % (2 * group) == 0 and 1 <= parts // (2 * group) <= 512, (b, parts)
+        else:
+            assert parts % (b * 32) == 0, (b, parts)
+            assert 2 <= parts // (b * 32) <= window // 256, (b, parts)
     assert swa.swa_decode_workspace_size(cache(window=window, dtype=swa.SWA_DTYPE_F32, n_kv_heads=hkv), 1, 32) == 0
 
 

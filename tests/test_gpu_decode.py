@@ -231,3 +231,72 @@ def test_mask_extraction_small_head_dims(d, window, group, fused):
         exp, cnt = expected_hist(p, window, d)
         for h in sorted({0, group - 1, group % 32, 31}):
             assert np.array_equal(np.rint(got[b, h].astype(np.float64) * cnt), exp), (d, p, h)
+
+
+def stream_positions(batch, seed):
+    """Positions for the stream plan: 0, 1, the window edges and log-uniform contexts up to
+    8 windows, in a shuffled order so that short and long pairs alternate in the slot stream."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 4095, 4096, 30000][:batch]
+    rest = np.exp(rng.uniform(np.log(2), np.log(32768), batch - len(fixed))).astype(int).tolist()
+    pos = fixed + rest
+    rng.shuffle(pos)
+    return [int(p) for p in pos]
+
+
+@pytest.mark.parametrize("group,d,batch", [(4, 128, 8), (8, 128, 64), (2, 128, 5), (4, 64, 20), (8, 16, 33),
+                                           (2, 16, 1)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_stream_plan_ragged_contexts(group, d, batch, fused):
+    """At most 64 sequences on the matrix-core kernel: the stream plan cuts the batch's
+    valid slots into equal workgroup ranges, which split pairs at arbitrary slots and
+    hold several short pairs each.  Output against the oracle; the fused step's cache
+    rows bit for bit."""
+    hkv = 32 // group
+    pos = stream_positions(batch, 600 + 7 * group + d + batch)
+    wl = make_workload("stream", 610 + group + d + batch, [(p, 1) for p in pos], window=4096, n_q_heads=32,
+                       n_kv_heads=hkv, head_dim=d, dtype="bf16", cache_rows=list(reversed(range(batch))))
+    cache = poisoned_cache(batch, hkv, 4096, d, "bf16")
+    nb = swa.swa_decode_workspace_size(cache, batch, 32)
+    assert nb > 0 and nb % (2 * group * (d + 2) * 4) == 0 and nb // (2 * group * (d + 2) * 4) <= 512
+    write_history(cache, wl)
+    if fused:
+        t = torch()
+        out = t.full((batch, 32, d), float("nan"), dtype=t.bfloat16, device="cuda")
+        ws = t.empty(nb, dtype=t.uint8, device="cuda")
+        kn, vn = dev(wl.k_new, "bf16"), dev(wl.v_new, "bf16")
+        swa.swa_decode_step(cache, swa.Batch([1] * batch, pos, wl.cache_idx), dev(wl.q, "bf16"), 32, kn, vn,
+                            wl.scale, out, ws, nb)
+        t.cuda.synchronize()
+        for b, p in enumerate(pos):
+            row = wl.cache_idx[b]
+            assert t.equal(cache.k[row, :, p % 4096].view(t.int16), kn[b].view(t.int16)), (b, p)
+            assert t.equal(cache.v[row, :, p % 4096].view(t.int16), vn[b].view(t.int16)), (b, p)
+    else:
+        out = run_decode(wl, cache)
+    check_close(host_f32(out, "bf16"), oracle_all(wl), "bf16", f"stream G={group} d={d} B={batch} fused={fused}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_stream_plan_mask_extraction_at_64_sequences(fused):
+    """64 sequences with 4 KV heads (G = 8), the largest stream batch: every slot of every
+    window counted exactly once, whatever range boundary or new-token slot it falls on."""
+    group, batch = 8, 64
+    rng = np.random.default_rng(77)
+    positions = MASK_POSITIONS + [int(p) for p in rng.integers(0, 20000, batch - len(MASK_POSITIONS))]
+    wl = mask_workload(positions, group, seed=978)
+    cache = poisoned_cache(batch, 32 // group, 4096, 128, "bf16")
+    nb = swa.swa_decode_workspace_size(cache, batch, 32)
+    assert nb > 0 and nb % (2 * group * 130 * 4) == 0
+    write_history(cache, wl)
+    t = torch()
+    bt = swa.Batch([1] * batch, positions, list(range(batch)))
+    q, kn, vn = dev(wl.q, "bf16"), dev(wl.k_new, "bf16"), dev(wl.v_new, "bf16")
+    out = t.full((batch, 32, 128), float("nan"), dtype=t.bfloat16, device="cuda")
+    ws = t.empty(nb, dtype=t.uint8, device="cuda")
+    if fused:
+        swa.swa_decode_step(cache, bt, q, 32, kn, vn, wl.scale, out, ws, nb)
+    else:
+        swa.swa_cache_write(cache, bt, kn, vn)
+        swa.swa_decode(cache, bt, q, 32, wl.scale, out, ws, nb)
+    assert_mask_histograms(host_f32(out, "bf16"), wl, group, f"stream B=64 fused={fused}")
