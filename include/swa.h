@@ -182,7 +182,7 @@ int swa_prefill_chunk_no_tile_skip(const swa_cache *cache, const swa_batch *batc
  *     part): num_seqs * n_q_heads * S * (head_dim + 2) * 4 bytes,
  *     2 <= S <= window / 256;
  *   - stream (bf16 on the matrix-core kernel -- G >= 2, or head_dim < 128 --
- *     with at most 64 sequences): the valid slots of the whole batch in equal
+ *     with 2 to 64 sequences): the valid slots of the whole batch in equal
  *     ranges, one per workgroup, which leaves at most two partials of the G
  *     query heads of a KV head: N * 2 * G * (head_dim + 2) * 4 bytes for
  *     N <= 512 workgroups.

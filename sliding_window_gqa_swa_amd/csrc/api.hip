@@ -145,12 +145,13 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   len = (len + 31) / 32 * 32;
   splits = (window + len - 1) / len;
   if (splits == 1) return pl;
-  if (!valu && num_seqs <= kStreamMaxSeqs && window <= (1 << 21)) {
+  if (!valu && num_seqs >= 2 && num_seqs <= kStreamMaxSeqs && window <= (1 << 21)) {
     // Too few rings to fill the chip one workgroup each: the matrix-core
     // kernel runs in stream mode, where every workgroup takes an equal share
     // of the batch's valid slots whatever each sequence's context length,
-    // with at most two partial results per workgroup.
-    const int64_t wg = std::min<int64_t>(target_wg, (pairs * window + kStreamMinRows - 1) / kStreamMinRows);
+    // with at most two partial results per workgroup.  (One sequence has the
+    // same context in every KV head: its split plan is balanced already.)
+    const int64_t wg = std::min<int64_t>(target_wg, (pairs * window + kStreamWgRows - 1) / kStreamWgRows);
     pl.stream_wg = (int32_t)wg;
     pl.acc_floats = (size_t)wg * 2 * group * head_dim;
     pl.workspace_bytes = (size_t)wg * 2 * group * (head_dim + 2) * sizeof(float);

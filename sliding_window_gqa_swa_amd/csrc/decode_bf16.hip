@@ -231,44 +231,20 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
   }
 }
 
-// Merge the per-split partials of each (sequence, query head).  The partials
-// are read kBatch at a time (independent loads in flight together); the sums
-// still run in split order.  An empty split (max -inf) has weight 0.
-// One thread per output element: blockDim = head_dim.
+// Merge the per-split partials of each (sequence, query head), in split
+// order (merge_partials).  One thread per output element, 64 ceil(head_dim /
+// 64) threads so that the waves are whole; threads past head_dim repeat the
+// last column and store nothing.
 __global__ __launch_bounds__(kD) void decode_combine_bf16_kernel(DecodeParams p) {
-  constexpr int kBatch = 8;
   const int bh = wg_x(), d = thread_x();
   const int D = p.cache.head_dim;
   const int S = p.splits;
+  const int dd = min(d, D - 1);
   const float *ml = p.ws_ml + (size_t)bh * S * 2;
-  const float *acc = p.ws_acc + (size_t)bh * S * D;
-  float mx = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
-    float mv[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) mv[i] = s0 + i < S ? ml[2 * (s0 + i)] : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) mx = fmaxf(mx, mv[i]);
-  }
-  float ls = 0.f, os = 0.f;
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
-    float mv[kBatch], lv[kBatch], av[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) {
-      const bool in = s0 + i < S;
-      mv[i] = in ? ml[2 * (s0 + i)] : -INFINITY;
-      lv[i] = in ? ml[2 * (s0 + i) + 1] : 0.f;
-      av[i] = in ? acc[(size_t)(s0 + i) * D + d] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) {
-      if (mv[i] == -INFINITY) continue;  // empty split or past the end
-      const float f = exp2f(mv[i] - mx);
-      ls += lv[i] * f;
-      os += av[i] * f;
-    }
-  }
-  ((uint16_t *)p.out)[(size_t)bh * D + d] = (uint16_t)pack_bf16(os / ls, 0.f);
+  const float *acc = p.ws_acc + (size_t)bh * S * D + dd;
+  const float o = merge_partials(
+      S, d & 63, [&](int j) { return ml + 2 * j; }, [&](int j) { return acc + (size_t)j * D; });
+  if (d < D) ((uint16_t *)p.out)[(size_t)bh * D + d] = (uint16_t)pack_bf16(o, 0.f);
 }
 
 template <int G>
@@ -285,7 +261,7 @@ hipError_t launch_g(const DecodeParams &p, hipStream_t stream) {
 hipError_t launch_decode_combine_bf16(const DecodeParams &p, hipStream_t stream) {
   if (p.seq.num_seqs == 0 || p.splits == 1) return hipSuccess;
   hipLaunchKernelGGL(decode_combine_bf16_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads),
-                     dim3((unsigned)p.cache.head_dim), 0, stream, p);
+                     dim3((unsigned)(64 * ((p.cache.head_dim + 63) / 64))), 0, stream, p);
   return hipGetLastError();
 }
 

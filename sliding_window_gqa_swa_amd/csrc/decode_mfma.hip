@@ -347,8 +347,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const int sp = wg_x() % splits;
     const int bg = wg_x() / splits;
     const int g = bg % hkv, b = bg / hkv;
+    // both per-sequence loads issued together (no branch on cache_idx between them)
+    const int32_t *ci = p.seq.cache_idx ? p.seq.cache_idx : p.seq.start_pos;
     const int pos = __builtin_amdgcn_readfirstlane(p.seq.start_pos[b]);
-    const int crow = p.seq.cache_idx ? __builtin_amdgcn_readfirstlane(p.seq.cache_idx[b]) : b;
+    const int ci_b = __builtin_amdgcn_readfirstlane(ci[b]);
+    const int crow = p.seq.cache_idx ? ci_b : b;
     const int n_valid = min(pos + 1, W);
     // uniform by construction; readfirstlane lets the compiler branch on them with scalar branches
     const int len = __builtin_amdgcn_readfirstlane(seq_split_len(n_valid, splits, p.split_len));
@@ -365,18 +368,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // piece by piece (one piece per pair it meets).  A piece that is a whole
     // pair gives final rows; the first and the last piece may be parts of pairs
     // and go to the workgroup's partial slots 0 and 1.  Every wave computes
-    // the same plan from the batch (at most 64 sequences, one per lane).
+    // the same plan from the batch (2 to 64 sequences, one per lane).
     const int lane = thread_x() & 63;
     const int ns = p.seq.num_seqs;
+    const int32_t *ci = p.seq.cache_idx ? p.seq.cache_idx : p.seq.start_pos;  // both loads issued together
     const int pos_l = lane < ns ? p.seq.start_pos[lane] : 0;
-    const int crow_l = lane < ns ? (p.seq.cache_idx ? p.seq.cache_idx[lane] : lane) : 0;
+    const int ci_l = lane < ns ? ci[lane] : 0;
+    const int crow_l = p.seq.cache_idx ? ci_l : lane;
     const int nv_l = lane < ns ? max(0, min(pos_l + 1, W)) : 0;
-    int incl = nv_l;  // inclusive prefix sum over the sequences
-#pragma unroll
-    for (int dl = 1; dl < 64; dl <<= 1) {
-      const int t = __shfl_up(incl, dl);
-      if (lane >= dl) incl += t;
-    }
+    const int incl = wave_incl_scan_i32(nv_l);  // inclusive prefix sum over the sequences
     const int total = hkv * __builtin_amdgcn_readlane(incl, 63);
     const int L = stream_range_rows(total, p.stream_wg);
     const int R0 = wg_x() * L;
@@ -387,6 +387,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     int b = __builtin_ffsll((long long)__builtin_amdgcn_ballot_w64(hkv * incl > R0)) - 1;
     int nvb = __builtin_amdgcn_readlane(nv_l, b);
     const int off = R0 - hkv * (__builtin_amdgcn_readlane(incl, b) - nvb);  // 0 <= off < hkv nvb
+    if (off < 0 || off >= hkv * nvb) return;  // cannot happen with a monotone prefix; no ring access outside it
     int g = off / nvb;
     int r_begin = off - g * nvb;
     int cur = R0;
@@ -413,10 +414,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 // Stream mode: merge the partial results of each (sequence, query head) whose
 // pair of slots spans several workgroups' ranges; pairs inside one range
 // already have their rows.  Each wave recomputes the decode kernel's plan from
-// the batch (lane i holds sequence i).  The partials come from workgroups
-// w0 .. w1 (slot 1 of w0 when the pair starts inside w0's range, else slot 0).
-// One thread per output element; 64 ceil(D / 64) threads, so that every wave
-// is whole for the sums over the batch.
+// the batch (lane i holds sequence i; the same prefix sum).  The partials come from workgroups
+// w0 .. w1 (slot 1 of w0 when the pair starts inside w0's range, else slot 0)
+// and are merged as in the split merge (decode_bf16.hip).  One thread per
+// output element; 64 ceil(D / 64) threads, so that every wave is whole for
+// the sums over the batch and the partials.
 __global__ __launch_bounds__(128) void decode_combine_stream_kernel(DecodeParams p) {
   const int bh = wg_x(), d = thread_x(), lane = d & 63;
   const int D = p.cache.head_dim, W = p.cache.window;
@@ -424,47 +426,23 @@ __global__ __launch_bounds__(128) void decode_combine_stream_kernel(DecodeParams
   const int b = bh / hq, h = bh % hq, g = h / G, hh = h % G;
   const int ns = p.seq.num_seqs;
   const int nv = lane < ns ? max(0, min(p.seq.start_pos[lane] + 1, W)) : 0;
-  const int total = hkv * __builtin_amdgcn_readfirstlane(wave_sum_i32(nv));
-  const int before = __builtin_amdgcn_readfirstlane(wave_sum_i32(lane < b ? nv : 0));
+  const int incl = wave_incl_scan_i32(nv);
+  const int total = hkv * __builtin_amdgcn_readlane(incl, 63);
   const int nvb = __builtin_amdgcn_readlane(nv, b);
-  if (nvb == 0 || d >= D) return;
+  const int before = __builtin_amdgcn_readlane(incl, b) - nvb;
+  if (nvb == 0) return;
+  const int dd = min(d, D - 1);  // threads past D repeat the last column and store nothing
   const int L = stream_range_rows(total, p.stream_wg);
   const int P = hkv * before + g * nvb;
   const int w0 = P / L, w1 = (P + nvb - 1) / L;
-  if (w0 == w1) return;
+  if (w0 == w1 || P < 0 || w1 >= p.stream_wg) return;  // (the last two cannot happen: slots in range)
   const int s0 = P == w0 * L ? 0 : 1;
-  // kBatch partials per round, loaded together (indexes clamped to w1, the
-  // extra values masked), merged into the running max and sums
-  constexpr int kBatch = 8;
-  float mx = -INFINITY, ls = 0.f, os = 0.f;
-  for (int wb = w0; wb <= w1; wb += kBatch) {
-    float mv[kBatch], lv[kBatch], av[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) {
-      const int w = min(wb + i, w1);
-      const size_t slot = ((size_t)w * 2 + (w == w0 ? s0 : 0)) * G + hh;
-      const float m_ld = p.ws_ml[slot * 2];
-      mv[i] = wb + i <= w1 ? m_ld : -INFINITY;
-      lv[i] = p.ws_ml[slot * 2 + 1];
-      av[i] = p.ws_acc[slot * D + d];
-    }
-    float bm = mx;
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) bm = fmaxf(bm, mv[i]);
-    if (bm == -INFINITY) continue;
-    const float r = exp2f(mx - bm);  // 0 while nothing is merged yet
-    ls *= r;
-    os *= r;
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) {
-      if (mv[i] == -INFINITY) continue;  // past w1, or a partial without keys
-      const float f = exp2f(mv[i] - bm);
-      ls += lv[i] * f;
-      os += av[i] * f;
-    }
-    mx = bm;
-  }
-  ((uint16_t *)p.out)[(size_t)bh * D + d] = (uint16_t)pack_bf16(os / ls, 0.f);
+  // partial j comes from workgroup w0 + j
+  auto slot_of = [&](int j) { return ((size_t)(w0 + j) * 2 + (j == 0 ? s0 : 0)) * G + hh; };
+  const float o = merge_partials(
+      w1 - w0 + 1, lane, [&](int j) { return p.ws_ml + slot_of(j) * 2; },
+      [&](int j) { return p.ws_acc + slot_of(j) * D + dd; });
+  if (d < D) ((uint16_t *)p.out)[(size_t)bh * D + d] = (uint16_t)pack_bf16(o, 0.f);
 }
 
 template <int G, int D>

@@ -95,11 +95,113 @@ __device__ __forceinline__ float sum_over_groups8(float x) {
   return add_pair32(add_pair16(x));
 }
 
-// Sum of an int over the 64 lanes of a wave (every lane must be active).
-__device__ __forceinline__ int wave_sum_i32(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+// Inclusive prefix sum of an int over the 64 lanes of a wave (every lane
+// active), on DPP: shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes
+// shifted in from outside the row add 0), then the total of row 0 added to
+// rows 1 and 3 (row_bcast:15) and the total of rows 0-1 to rows 2 and 3
+// (row_bcast:31).  Rows outside the row mask keep the old value 0.
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
+}
+
+// One DPP step of the float scans below: x's value from the lane Ctrl names
+// (row_shr:n or row_bcast), `ident` where that lane is outside the row or the
+// row is masked off.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_f32(float x, float ident) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, ident), __builtin_bit_cast(int, x),
+                                                               Ctrl, RowMask, 0xf, false));
+}
+// Maximum and sum of a float over the 64 lanes of a wave (every lane active),
+// as the scan of wave_incl_scan_i32 with max / add; the result (lane 63 of the
+// scan) is returned uniform.
+__device__ __forceinline__ float wave_max_f32(float x) {
+  const float ni = -INFINITY;
+  x = fmaxf(x, dpp_f32<0x111, 0xf>(x, ni));
+  x = fmaxf(x, dpp_f32<0x112, 0xf>(x, ni));
+  x = fmaxf(x, dpp_f32<0x114, 0xf>(x, ni));
+  x = fmaxf(x, dpp_f32<0x118, 0xf>(x, ni));
+  x = fmaxf(x, dpp_f32<0x142, 0xa>(x, ni));
+  x = fmaxf(x, dpp_f32<0x143, 0xc>(x, ni));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += dpp_f32<0x111, 0xf>(x, 0.f);
+  x += dpp_f32<0x112, 0xf>(x, 0.f);
+  x += dpp_f32<0x114, 0xf>(x, 0.f);
+  x += dpp_f32<0x118, 0xf>(x, 0.f);
+  x += dpp_f32<0x142, 0xa>(x, 0.f);
+  x += dpp_f32<0x143, 0xc>(x, 0.f);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+// Lane `i` (uniform) of a float.
+__device__ __forceinline__ float lane_f32(float x, int i) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
+}
+
+// Merge of n >= 1 partial results of one output row (unnormalised output
+// sums, running max in log2 units, weight sum): returns
+// sum_j w_j row_j[col] / sum_j w_j l_j with w_j = exp2(m_j - max_j m_j).
+// Called by every thread of whole waves, one thread per column col.
+// ml_at(j) points at partial j's (max, sum), row_at(j) at its value for this
+// thread's column.  Lane i handles the (max, sum) of partials i, i + 64, ...;
+// the first 64 pairs and the first kMergeBatch row values are loaded before
+// any arithmetic, so a merge of up to kMergeBatch partials waits for memory
+// once.  The max and the weight sum are wave reductions; each partial's
+// weight is broadcast to the threads that add its row, and the rows add in
+// partial order.  A partial whose max is -inf (no keys) has weight 0.
+constexpr int kMergeBatch = 8;
+template <class MlAt, class RowAt>
+__device__ __forceinline__ float merge_partials(int n, int lane, MlAt ml_at, RowAt row_at) {
+  float m0 = -INFINITY, l0 = 0.f;
+  if (lane < n) {
+    const float *q = ml_at(lane);
+    m0 = q[0];
+    l0 = q[1];
+  }
+  float a0[kMergeBatch];
+#pragma unroll
+  for (int i = 0; i < kMergeBatch; i++) a0[i] = *row_at(i < n ? i : n - 1);
+  float mx = m0;
+  for (int c0 = 64; c0 < n; c0 += 64)
+    if (c0 + lane < n) mx = fmaxf(mx, ml_at(c0 + lane)[0]);
+  mx = wave_max_f32(mx);
+  float ls = 0.f, os = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int cn = n - c0 < 64 ? n - c0 : 64;
+    float m = m0, l = l0;
+    if (c0 > 0) {
+      m = -INFINITY;
+      l = 0.f;
+      if (lane < cn) {
+        const float *q = ml_at(c0 + lane);
+        m = q[0];
+        l = q[1];
+      }
+    }
+    const float w = (lane < cn && m != -INFINITY) ? exp2f(m - mx) : 0.f;
+    ls += w * l;
+    for (int i0 = 0; i0 < cn; i0 += kMergeBatch) {
+      float av[kMergeBatch];
+      if (c0 == 0 && i0 == 0) {
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; i++) av[i] = a0[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; i++) av[i] = *row_at(c0 + (i0 + i < cn ? i0 + i : cn - 1));
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; i++)
+        if (i0 + i < cn) os += lane_f32(w, i0 + i) * av[i];
+    }
+  }
+  return os / wave_sum_f32(ls);
 }
 
 // Workgroups are dispatched to the XCDs round-robin (id mod 8).  Give each XCD

@@ -95,9 +95,12 @@ __device__ __forceinline__ int seq_split_len(int n_valid, int splits, int plan_l
 // Stream mode of the matrix-core decode (small batches): the valid slots of
 // all (sequence, KV head) pairs, laid end to end sequence-major, are cut into
 // stream_wg contiguous ranges of equal length, one per workgroup, so that
-// sequences of different context lengths cost the same per slot.  The range
-// length is a multiple of 32, at least kStreamMinRows; total_rows <= 2^30.
-constexpr int kStreamMinRows = 256;
+// sequences of different context lengths cost the same per slot.  The plan
+// sizes the grid for ranges of kStreamWgRows slots of full windows; the range
+// length is a multiple of 32, at least kStreamMinRows, so short contexts still
+// spread over many workgroups.  total_rows <= 2^30.
+constexpr int kStreamWgRows = 256;
+constexpr int kStreamMinRows = 128;
 constexpr int kStreamMaxSeqs = 64;  // one wave scans the batch
 __host__ __device__ __forceinline__ int stream_range_rows(int total_rows, int stream_wg) {
   int len = (total_rows + stream_wg - 1) / stream_wg;

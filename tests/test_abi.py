@@ -221,9 +221,11 @@ def test_workspace_plan():
     assert swa.swa_decode_workspace_size(c, 64, 32) == 0
     # 8 sequences (G = 4): stream mode, 512 workgroups x 2 partials x 4 heads x (D + 2) floats
     assert swa.swa_decode_workspace_size(c, 8, 32) == 512 * 2 * 4 * (128 + 2) * 4
-    # one sequence, one KV head, G = 2: 4096 slots give 16 ranges of 256
-    c1 = cache(window=4096, n_cache=1, n_kv_heads=1)
-    assert swa.swa_decode_workspace_size(c1, 1, 2) == 16 * 2 * 2 * (128 + 2) * 4
+    # two sequences, one KV head, G = 2: 2 x 4096 slots give 32 ranges of 256
+    c1 = cache(window=4096, n_cache=2, n_kv_heads=1)
+    assert swa.swa_decode_workspace_size(c1, 2, 2) == 32 * 2 * 2 * (128 + 2) * 4
+    # one sequence (the same context in every KV head): split plan, 16 parts of 256 slots
+    assert swa.swa_decode_workspace_size(c1, 1, 2) == 1 * 2 * 16 * (128 + 2) * 4
     # 65 sequences x 4 KV heads (G = 8): past the stream batch limit, split plan
     c8 = cache(window=4096, n_cache=65, n_kv_heads=4)
     sz8 = swa.swa_decode_workspace_size(c8, 65, 32)
@@ -244,8 +246,8 @@ def test_workspace_plan():
 def test_workspace_size_guarantees(group, window, head_dim):
     """The guarantees stated with swa_decode_workspace_size: the size is a whole
     number of partial results of head_dim + 2 floats, laid out by one of the two
-    plans -- split (num_seqs x n_q_heads x S, 2 <= S <= W / 256) or stream (at
-    most 64 sequences, matrix-core kernel: N x 2 x G with N <= 512) -- none for
+    plans -- split (num_seqs x n_q_heads x S, 2 <= S <= W / 256) or stream (2 to
+    64 sequences, matrix-core kernel: N x 2 x G with N <= 512) -- none for
     W < 512 or once the batch alone gives 2048 (sequence, KV head) pairs, and
     never more than the stated maximum."""
     hkv = 32 // group
@@ -263,7 +265,7 @@ def test_workspace_size_guarantees(group, window, head_dim):
         part = (head_dim + 2) * 4
         assert sz % part == 0, (b, sz)
         parts = sz // part
-        if not on_valu and b <= 64:
+        if not on_valu and 2 <= b <= 64:
             assert parts % (2 * group) == 0 and 1 <= parts // (2 * group) <= 512, (b, parts)
         else:
             assert parts % (b * 32) == 0, (b, parts)
