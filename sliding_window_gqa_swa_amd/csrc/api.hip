@@ -133,8 +133,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   // Workgroups per launch to aim for.  The VALU kernel (G = 1) wants >= ~2048
   // (8 per CU).  The matrix-core kernel (G >= 2) holds 2 workgroups per CU, so
   // 512 fill the chip once: 64 sequences x 8 KV heads then take one split per
-  // ring and need no merge launch.  A split keeps >= 256 slots either way, so
-  // that each wave streams several 16 KiB steps.
+  // ring and need no merge launch.  A split of a full window keeps >= 256
+  // slots either way, so that each wave streams several 16 KiB steps; smaller
+  // batches on the matrix-core kernel go to the stream plan below.
   const int64_t pairs = (int64_t)num_seqs * n_kv_heads;
   const int32_t group = n_q_heads / n_kv_heads;
   const bool valu = decode_on_valu(group, head_dim);

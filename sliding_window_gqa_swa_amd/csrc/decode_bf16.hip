@@ -16,7 +16,8 @@
 // 8 (and head_dim 16 / 64 at any G) run on the matrix cores (decode_mfma.hip),
 // because the per-head VALU work here grows with G.  The template still
 // handles G <= 8, and the split merge (combine kernel) below serves both
-// kernels at every head_dim.
+// kernels' split plans at every head_dim (the matrix-core kernel's stream plan
+// has its own merge, on the same merge_partials routine).
 //
 // Design (HBM-bound: 4 FLOP per byte of K/V):
 //   * One workgroup = (sequence, KV head, split of the window): 4 waves.  All
