@@ -181,11 +181,11 @@ int swa_prefill_chunk_no_tile_skip(const swa_cache *cache, const swa_batch *batc
  *   - split: each window in S parts, one partial per (sequence, query head,
  *     part): num_seqs * n_q_heads * S * (head_dim + 2) * 4 bytes,
  *     2 <= S <= window / 256;
- *   - stream (bf16 on the matrix-core kernel -- G >= 2, or head_dim < 128 --
- *     with 2 to 64 sequences): the valid slots of the whole batch in equal
- *     ranges, one per workgroup, which leaves at most two partials of the G
- *     query heads of a KV head: N * 2 * G * (head_dim + 2) * 4 bytes for
- *     N <= 512 workgroups.
+ *   - stream (bf16 on the matrix-core kernel -- G >= 2 at head_dim 128, any
+ *     G at head_dim 64 -- with 2 to 64 sequences): the valid slots of the
+ *     whole batch in equal ranges, one per workgroup, which leaves at most two
+ *     partials of the G query heads of a KV head: N * 2 * G * (head_dim + 2)
+ *     * 4 bytes for N <= 512 workgroups.
  * Guarantees: the size depends only on the arguments of this call; it is 0 for
  * SWA_DTYPE_F32, for window < 512 and when num_seqs * n_kv_heads >= 2048; it
  * never exceeds SWA_DECODE_WORKSPACE_MAX_BYTES.

@@ -146,12 +146,15 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t n_kv_heads, int32_t n_q_heads, 
   len = (len + 31) / 32 * 32;
   splits = (window + len - 1) / len;
   if (splits == 1) return pl;
-  if (!valu && num_seqs >= 2 && num_seqs <= kStreamMaxSeqs && window <= (1 << 21)) {
+  if (!valu && head_dim >= 64 && num_seqs >= 2 && num_seqs <= kStreamMaxSeqs &&
+      pairs * window <= (int64_t(1) << 30)) {
     // Too few rings to fill the chip one workgroup each: the matrix-core
     // kernel runs in stream mode, where every workgroup takes an equal share
     // of the batch's valid slots whatever each sequence's context length,
     // with at most two partial results per workgroup.  (One sequence has the
-    // same context in every KV head: its split plan is balanced already.)
+    // same context in every KV head: its split plan is balanced already.  At
+    // head_dim 16 the whole launch is short and latency-bound, and the stream
+    // prologue and piece changes cost more than the balance gains.)
     const int64_t wg = std::min<int64_t>(target_wg, (pairs * window + kStreamWgRows - 1) / kStreamWgRows);
     pl.stream_wg = (int32_t)wg;
     pl.acc_floats = (size_t)wg * 2 * group * head_dim;

@@ -98,7 +98,7 @@ __device__ __forceinline__ int seq_split_len(int n_valid, int splits, int plan_l
 // sequences of different context lengths cost the same per slot.  The plan
 // sizes the grid for ranges of kStreamWgRows slots of full windows; the range
 // length is a multiple of 32, at least kStreamMinRows, so short contexts still
-// spread over many workgroups.  total_rows <= 2^30.
+// spread over many workgroups.  total_rows <= 2^30 (the plan checks pairs x W).
 constexpr int kStreamWgRows = 256;
 constexpr int kStreamMinRows = 128;
 constexpr int kStreamMaxSeqs = 64;  // one wave scans the batch

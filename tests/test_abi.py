@@ -247,7 +247,7 @@ def test_workspace_size_guarantees(group, window, head_dim):
     """The guarantees stated with swa_decode_workspace_size: the size is a whole
     number of partial results of head_dim + 2 floats, laid out by one of the two
     plans -- split (num_seqs x n_q_heads x S, 2 <= S <= W / 256) or stream (2 to
-    64 sequences, matrix-core kernel: N x 2 x G with N <= 512) -- none for
+    64 sequences, matrix-core kernel at head_dim >= 64: N x 2 x G with N <= 512) -- none for
     W < 512 or once the batch alone gives 2048 (sequence, KV head) pairs, and
     never more than the stated maximum."""
     hkv = 32 // group
@@ -265,7 +265,7 @@ def test_workspace_size_guarantees(group, window, head_dim):
         part = (head_dim + 2) * 4
         assert sz % part == 0, (b, sz)
         parts = sz // part
-        if not on_valu and 2 <= b <= 64:
+        if not on_valu and head_dim >= 64 and 2 <= b <= 64:
             assert parts % (2 * group) == 0 and 1 <= parts // (2 * group) <= 512, (b, parts)
         else:
             assert parts % (b * 32) == 0, (b, parts)

@@ -244,8 +244,8 @@ def stream_positions(batch, seed):
     return [int(p) for p in pos]
 
 
-@pytest.mark.parametrize("group,d,batch", [(4, 128, 8), (8, 128, 64), (2, 128, 5), (4, 64, 20), (8, 16, 33),
-                                           (2, 16, 2)])
+@pytest.mark.parametrize("group,d,batch", [(4, 128, 8), (8, 128, 64), (2, 128, 5), (4, 64, 20), (8, 64, 33),
+                                           (2, 64, 2), (1, 64, 7)])
 @pytest.mark.parametrize("fused", [False, True])
 def test_stream_plan_ragged_contexts(group, d, batch, fused):
     """2 to 64 sequences on the matrix-core kernel: the stream plan cuts the batch's
