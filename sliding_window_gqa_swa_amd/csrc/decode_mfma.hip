@@ -12,7 +12,8 @@
 // so it runs on v_mfma_f32_16x16x32_bf16 (the G heads padded to 16 columns)
 // instead of per-head VALU dot products, which cost more per byte as G grows:
 //   * Split mode: one workgroup = (sequence, KV head, split of the window),
-//     4 waves; a wave takes 32-key steps r0 = split start + 32 w + 128 j.
+//     4 waves (16 at head_dim 16); a wave takes 32-key steps
+//     r0 = split start + 32 w + 32 kWaves j.
 //   * Stream mode (batches too small to fill the chip with whole windows):
 //     the valid slots of all (sequence, KV head) pairs are laid end to end and
 //     cut into equal ranges, one per workgroup, which attends to its range one
@@ -43,8 +44,6 @@
 namespace swa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;                  // keys per wave step
 constexpr float kRescaleSlack = 8.0f;      // log2 units, as in the prefill
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
@@ -75,6 +74,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // groups.
 template <int D>
 struct RowGeo {
+  // waves per workgroup: at head_dim 16 a row is 32 bytes, so more waves keep
+  // enough bytes in flight (the kernel is small in registers and LDS there)
+  static constexpr int kWaves = D == 16 ? 16 : 4;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kRowB = 2 * D;
   static constexpr int kVBufB = kStep * kRowB;         // one wave step of V rows
   static constexpr int kC = D / 8;
@@ -90,7 +93,7 @@ struct RowGeo {
 };
 
 template <int D>
-using VBuf = unsigned char[kWaves][RowGeo<D>::kVBufB];
+using VBuf = unsigned char[RowGeo<D>::kWaves][RowGeo<D>::kVBufB];
 
 // Where the result of one attended range goes: the final bf16 rows of out
 // (acc == nullptr), or partial results -- unnormalised output sums, running
@@ -113,6 +116,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, VBuf<D> &vbu
   using Rg = RowGeo<D>;
   constexpr int kD = D, kRowB = Rg::kRowB, kVBufB = Rg::kVBufB, kC = Rg::kC, kRpl = Rg::kRpl;
   constexpr int kKS = Rg::kKS, kDB = Rg::kDB;
+  constexpr int kWaves = Rg::kWaves, kThreads = Rg::kThreads;
   static_assert(kWaves * G * (kD + 2) * 4 <= kWaves * kVBufB, "the wave merge fits in vbuf_a");
 
   const int tid = thread_x(), lane = tid & 63;
@@ -335,10 +339,10 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, VBuf<D> &vbu
 }
 
 template <int G, int D, bool kStream>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(RowGeo<D>::kThreads) void decode_mfma_kernel(DecodeParams p) {
   // two V buffers per wave, as two objects; after a range vbuf_a holds the merge
-  __shared__ __attribute__((aligned(16))) unsigned char vbuf_a[kWaves][RowGeo<D>::kVBufB];
-  __shared__ __attribute__((aligned(16))) unsigned char vbuf_b[kWaves][RowGeo<D>::kVBufB];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf_a[RowGeo<D>::kWaves][RowGeo<D>::kVBufB];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf_b[RowGeo<D>::kWaves][RowGeo<D>::kVBufB];
   const int hkv = p.cache.n_kv_heads;
   const int W = p.cache.window;
   if constexpr (!kStream) {
@@ -449,7 +453,7 @@ template <int G, int D>
 hipError_t launch_gd(const DecodeParams &p, hipStream_t stream) {
   if (p.stream_wg > 0) {
     if (p.seq.num_seqs > kStreamMaxSeqs) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_mfma_kernel<G, D, true>), dim3((unsigned)p.stream_wg), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, D, true>), dim3((unsigned)p.stream_wg), dim3(RowGeo<D>::kThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_stream_kernel, dim3((unsigned)p.seq.num_seqs * p.n_q_heads),
@@ -457,7 +461,7 @@ hipError_t launch_gd(const DecodeParams &p, hipStream_t stream) {
     return hipGetLastError();
   }
   const unsigned n_wg = (unsigned)p.seq.num_seqs * p.cache.n_kv_heads * p.splits;
-  hipLaunchKernelGGL((decode_mfma_kernel<G, D, false>), dim3(n_wg), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, D, false>), dim3(n_wg), dim3(RowGeo<D>::kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine_bf16(p, stream);
