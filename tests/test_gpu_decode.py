@@ -5,6 +5,8 @@ generated one at a time (paragraph "Pre-fill and Chunking"); each reads the W
 most recent positions from the rolling buffer (paragraphs "Sliding Window
 Attention", "Rolling Buffer Cache").  The new token is written first.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -300,3 +302,61 @@ def test_stream_plan_mask_extraction_at_64_sequences(fused):
         swa.swa_cache_write(cache, bt, kn, vn)
         swa.swa_decode(cache, bt, q, 32, wl.scale, out, ws, nb)
     assert_mask_histograms(host_f32(out, "bf16"), wl, group, f"stream B=64 fused={fused}")
+
+
+def long_window_cache(positions, window, d=128):
+    """Rings of one KV head holding, for each sequence, the window ending at its position:
+    K = 0 and V of position j = one-hot(j mod 64) + one-hot(64 + (j // 256) mod 64)."""
+    t = torch()
+    n = len(positions)
+    k = t.zeros((n, 1, window, d), dtype=t.bfloat16, device="cuda")
+    v = t.zeros((n, 1, window, d), dtype=t.bfloat16, device="cuda")
+    slots = t.arange(window, device="cuda", dtype=t.int64)
+    for b, pos in enumerate(positions):
+        j = pos - t.remainder(pos - slots, window)          # position held by each slot
+        valid = j >= 0
+        rows = slots[valid]
+        jj = j[valid]
+        v[b, 0, rows, jj % 64] = 1.0
+        v[b, 0, rows, 64 + (jj // 256) % 64] = 1.0
+    return swa.Cache(k, v)
+
+
+def expected_long_window(pos, window):
+    lo = max(0, pos - window + 1)
+    j = np.arange(lo, pos + 1)
+    o = np.zeros(128)
+    np.add.at(o, j % 64, 1.0)
+    np.add.at(o, 64 + (j // 256) % 64, 1.0)
+    return o / len(j)
+
+
+@pytest.mark.parametrize("positions", [[256 * 200 - 1], [256 * 300 - 1, 256 * 280 - 1], [30000, 256 * 300 - 1]])
+def test_merge_of_more_than_64_partials(positions):
+    """W = 32768 with one KV head (G = 2): one sequence takes the split plan with 128 parts;
+    two sequences take the stream plan, where each window spans ~128 workgroup ranges (the
+    second case starts the second window inside a range).  Both merges then loop over their
+    partials in chunks of 64.  Q = K = 0 weighs every key equally, and with windows that end
+    at 256k - 1 every bin of the one-hot V holds exactly 512 of the 32768 keys: the output is
+    exactly 1/64.  One 256-slot piece dropped or counted twice changes it."""
+    t = torch()
+    W, hq, d = 32768, 2, 128
+    n = len(positions)
+    cache = long_window_cache(positions, W, d)
+    nb = swa.swa_decode_workspace_size(cache, n, hq)
+    if n == 1:
+        assert nb == 128 * hq * (d + 2) * 4         # split plan: 128 parts of 256 slots
+    else:
+        assert nb == 256 * 2 * hq * (d + 2) * 4     # stream plan: 256 workgroups, ranges of 256 slots
+    ws = t.empty(nb, dtype=t.uint8, device="cuda")
+    q = t.zeros((n, hq, d), dtype=t.bfloat16, device="cuda")
+    out = t.full((n, hq, d), float("nan"), dtype=t.bfloat16, device="cuda")
+    swa.swa_decode(cache, swa.Batch([1] * n, positions, list(range(n))), q, hq, 1.0 / math.sqrt(d), out, ws, nb)
+    got = host_f32(out, "bf16")
+    for b, pos in enumerate(positions):
+        exp = expected_long_window(pos, W)
+        for h in range(hq):
+            if (pos + 1) % 256 == 0 and pos + 1 >= W:
+                assert np.array_equal(got[b, h], exp.astype(np.float32)), (pos, h)
+            else:
+                assert np.abs(got[b, h] - exp).max() <= 2e-3, (pos, h)
