@@ -22,7 +22,7 @@
  *     the caller, except the fields prefixed h_ (host pointers).  The library
  *     allocates nothing, keeps no pointer after returning and has no global
  *     mutable state; calls are re-entrant.  (The one exception is
- *     swa_decode_step_noalloc, whose split partials live in a device array of
+ *     swa_decode_step_noalloc, whose merge partials live in a device array of
  *     the library's own; see there.)
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *     null stream) and never synchronizes.  Buffers must stay alive until the
@@ -238,7 +238,7 @@ int swa_decode_step(const swa_cache *cache, const swa_batch *batch,
  * swa_decode_step without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, validation and result
- * as swa_decode_step -- output and cache bit for bit -- but the split
+ * as swa_decode_step -- output and cache bit for bit -- but the merge
  * partials go to a device array inside the library of
  * SWA_DECODE_WORKSPACE_MAX_BYTES bytes (8 MiB), one per GPU, held until the
  * process ends.  It calls no allocator.  The first call on a GPU looks up the

@@ -274,7 +274,7 @@ def swa_decode_step(cache, batch, q, n_q_heads: int, k_new, v_new, sm_scale: flo
 
 def swa_decode_step_noalloc(cache, batch, q, n_q_heads: int, k_new, v_new, sm_scale: float, out, stream=None,
                             check: bool = True) -> int:
-    """swa_decode_step with the split partials in the library's own device array (no workspace argument)."""
+    """swa_decode_step with the merge partials in the library's own device array (no workspace argument)."""
     c, b = _as_cache(cache), _as_batch(batch)
     code = lib().swa_decode_step_noalloc(ctypes.byref(c), ctypes.byref(b), _ptr(q), int(n_q_heads), _ptr(k_new),
                                          _ptr(v_new), float(sm_scale), _ptr(out), _stream(stream))
