@@ -11,7 +11,10 @@ already resident in HBM:
                          4096-slot rings, 1 GiB of K/V).
 The headline value is the prefill's band TFLOP/s (algorithmic FLOPs: 4 * D *
 Hq * sum_i |J(i)|); the decode's K/V GB/s is reported beside it.  Each stage
-is timed with HIP events on the stream it runs on.
+is timed with HIP events on the stream it runs on.  Before the warm-up steps,
+untimed steps run for 0.2 s: from idle, the part needs a few tens of
+milliseconds of load to reach the clock it holds under it, and every timing of
+the suite is preceded by 0.1 s of the same.
 
 The suite (default on) times the other workloads: causal attention and the
 prefill without its band tile skip at 16K tokens, 4 x 32768 tokens chunked
@@ -20,7 +23,7 @@ G = 1, per-token decode steps, and a 32-layer ring.  The CPU baseline is the
 fp64 oracle on the host cores: the whole 16K prefill, plus stated samples of
 the other workloads.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-suite]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-suite]
     python bench.py --only chunked|mixed|decode_g1   # one suite workload (for profilers)
 """
 from __future__ import annotations
@@ -234,11 +237,35 @@ def cpu_leg_mixed(wp, wd, rows_per_seq=256):
 
 # ----------------------------------------------------------------------------- timing helpers
 
-def time_ms(fn, reps: int) -> float:
-    """Mean milliseconds of `fn` over `reps` launches, HIP events on the current stream."""
+SETTLE_S = 0.2  # untimed load before every measurement (the clock ramp from idle takes ~40 ms)
+SETTLE_S_SUITE = 0.1
+
+
+def settle(fn, seconds: float) -> int:
+    """Run `fn` repeatedly for `seconds` of wall time, untimed, and return the launch count.
+
+    From idle, the part takes a few tens of milliseconds of load to reach the clock it holds
+    under that load. The 16K prefill takes ~0.87 ms per launch over its first 20 launches and
+    0.79 ms from about the 50th on (one box, back-to-back launches). A synchronisation every
+    8 launches keeps the host from queueing far ahead of the GPU, so the wall time tracks the
+    GPU's busy time."""
     import torch
-    fn()
-    torch.cuda.synchronize()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n
+
+
+def time_ms(fn, reps: int) -> float:
+    """Mean milliseconds of `fn` over `reps` launches, HIP events on the current stream
+    (after `settle`)."""
+    import torch
+    settle(fn, SETTLE_S_SUITE)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -252,7 +279,7 @@ def time_ms_cold(fn, reps: int, flush) -> float:
     """Mean milliseconds of `fn`, each launch timed alone after `flush` has
     overwritten the 256 MB Infinity Cache (so no input is served from it)."""
     import torch
-    fn()
+    settle(lambda: (flush(), fn()), SETTLE_S_SUITE)
     total = 0.0
     for _ in range(reps):
         flush()
@@ -536,8 +563,8 @@ def decode_step_latency(dcache, positions, rows, dq, dk, dv, scale, reps: int, s
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
     ap.add_argument("--only", choices=["chunked", "mixed", "decode_g1"],
@@ -603,18 +630,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(ev):
-        ev[0].record()
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        rec(0)
         swa.swa_prefill_chunk(pcache, pbatch, pq, HQ, pk, pv, wp.scale, pout)
-        ev[1].record()
+        rec(1)
         swa.swa_cache_write(pcache, pbatch, pk, pv)
-        ev[2].record()
+        rec(2)
         swa.swa_cache_write(dcache, dbatch, dk, dv)
-        ev[3].record()
+        rec(3)
         swa.swa_decode(dcache, dbatch, dq, HQ, wd.scale, dout, ws, ws_bytes)
-        ev[4].record()
+        rec(4)
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    # untimed steps until the clock has settled, then the warm-up steps, then the timed ones
+    settle_steps = settle(step, SETTLE_S)
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -643,6 +673,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": SETTLE_S, "steps": settle_steps,
+                   "why": "untimed steps before the warm-up: from idle the clock takes a few tens of ms of load to settle"},
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
