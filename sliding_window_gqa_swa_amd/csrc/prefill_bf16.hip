@@ -38,9 +38,11 @@
 //     mask code.  Keys outside the band are never read from outside it: their
 //     rows are loaded from the nearest key of the band (always written data)
 //     and masked, so unwritten cache slots cannot reach the arithmetic.
+//   * The matrix half-step is an explicit pipeline over operand fragments:
+//     each V or K fragment is read from LDS four fragments before the two
+//     MFMAs that use it, and every step of the pipeline is pinned in place.
 //   * Online softmax in fp32 with exp2.  The softmax half-step competes with
-//     the other wave's MFMAs for the VALU issue port, so its instruction count
-//     per tile bounds the matrix rate; it is kept small:
+//     the other wave's MFMAs for the VALU issue port; it is kept small:
 //       - the score accumulators start at -M (the running max of q.k), so
 //         a weight is exp2(c * accumulator), one multiply per score;
 //       - the row sums are an MFMA of the bf16 weights with a ones operand,
@@ -258,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   f32x4 sa[4][2];                       // S^T of the tile in flight: 4 key blocks x 2 query blocks
   u32x4 pw[2][2];                       // P^T (bf16 pairs) of the softmaxed tile: [32-key slice][qb]
 
-  // S^T - M = K Q^T + negm (the order of LDS reads and MFMAs is set by the
-  // half-step schedule)
+  // S^T - M = K Q^T + negm (the prologue's first tile; the matrix half-step
+  // below computes the same for the tiles after it)
   auto qk = [&](const unsigned char *kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int kbi = 0; kbi < 4; kbi++)
@@ -288,28 +290,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     w[2] = __builtin_bit_cast(u32x2, v2)[0];
     w[3] = __builtin_bit_cast(u32x2, v2)[1];
     return __builtin_bit_cast(bf16x8, w);
-  };
-
-  // row sums and O^T += V^T P^T (order of reads and MFMAs as for qk)
-  auto pv = [&](const unsigned char *vbase) __attribute__((always_inline)) {
-    // row sums of exactly the bf16 weights that enter P V; these MFMAs need no
-    // LDS data, so they go first, under the latency of the first operand reads
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++) {
-      lsum[0] = mfma16(ones, __builtin_bit_cast(bf16x8, pw[kk][0]), lsum[0]);
-      lsum[1] = mfma16(ones, __builtin_bit_cast(bf16x8, pw[kk][1]), lsum[1]);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++) {
-      const bf16x8 p0 = __builtin_bit_cast(bf16x8, pw[kk][0]);
-      const bf16x8 p1 = __builtin_bit_cast(bf16x8, pw[kk][1]);
-#pragma unroll
-      for (int db = 0; db < kDB; db++) {
-        const bf16x8 vf = vread(vbase, kk, db);
-        o[db][0] = mfma16(vf, p0, o[db][0]);
-        o[db][1] = mfma16(vf, p1, o[db][1]);
-      }
-    }
   };
 
   // mask (edge tiles), online softmax, P^T as bf16 into pw.
@@ -399,25 +379,50 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int n_diag_free = (q0 - kBN + 1 - kt0) >= 0 ? (q0 - kBN + 1 - kt0) / kBN + 1 : 0;
   const int t_mid_end = max(n_lead, min(n_tiles, n_diag_free));
 
-  // Order of the matrix half-step's 48 LDS reads (32 V, then 16 K) and 68
-  // MFMAs (4 row sums, 32 PV, then 32 QK): eight reads first, then the four
-  // row-sum MFMAs, then two MFMAs and two reads alternately, so reads run
-  // about four MFMA pairs ahead of their consumers and the K reads of the next
-  // QK overlap the tail of PV.  (The compiler may
-  // still move the last QK MFMAs past the closing barrier; measured, that
-  // beats keeping them inside.)
-  auto schedule_matrix_half_step = [&]() __attribute__((always_inline)) {
-    constexpr int kReads = 4 * kDB + 4 * kKS;               // V reads, then K reads
-    constexpr int kMfma = 4 * kDB + 8 * kKS;                // P V, then Q K
-    constexpr int kLead = kReads < 8 ? kReads : 8, kPairs = (kReads - kLead) / 2;
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // 0x100: LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // the row-sum MFMAs
+  // The matrix half-step M_t = { row sums; O^T += V^T P^T(t); S^T(t+1) - M =
+  // K(t+1) Q^T + negm } as a pipeline over operand fragments: first the 2 kDB V
+  // fragments (key slice kk, d-block db; two transposed reads each), then the
+  // 4 kKS K fragments (step ks, key block kbi; one read each), each feeding two
+  // MFMAs (query blocks 0 and 1).  Fragment f is read kFragLead fragments ahead
+  // of its MFMAs, the four row-sum MFMAs (no LDS operand) run under the latency
+  // of the first reads, and every iteration ends in a scheduling barrier, so
+  // the compiler keeps this order (its wait counts follow the reads).
+  constexpr int kFragLead = 4;
+  auto matrix_half_step = [&](const unsigned char *vbase, const unsigned char *kb, auto with_qk)
+                              __attribute__((always_inline)) {
+    constexpr int kNV = 2 * kDB;
+    constexpr int kNF = kNV + (decltype(with_qk)::value ? 4 * kKS : 0);
+    bf16x8 fr[kFragLead];
+    auto load = [&](int f) __attribute__((always_inline)) {
+      if (f < kNV) return vread(vbase, f / kDB, f % kDB);
+      const int g = f - kNV;
+      return *(const bf16x8 *)(kb + k_off[g / 4] + 16 * kRowB * (g % 4));
+    };
+    auto use = [&](int f, bf16x8 x) __attribute__((always_inline)) {
+      if (f < kNV) {
+        const int kk = f / kDB, db = f % kDB;
+        o[db][0] = mfma16(x, __builtin_bit_cast(bf16x8, pw[kk][0]), o[db][0]);
+        o[db][1] = mfma16(x, __builtin_bit_cast(bf16x8, pw[kk][1]), o[db][1]);
+      } else {
+        const int g = f - kNV, ks = g / 4, kbi = g % 4;
+        sa[kbi][0] = mfma16(x, qf[ks][0], ks == 0 ? negm[0] : sa[kbi][0]);
+        sa[kbi][1] = mfma16(x, qf[ks][1], ks == 0 ? negm[1] : sa[kbi][1]);
+      }
+    };
 #pragma unroll
-    for (int i = 0; i < kPairs; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // 0x008: MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int i = 0; i < kNF + kFragLead; i++) {
+      if (i >= kFragLead) use(i - kFragLead, fr[(i - kFragLead) % kFragLead]);
+      if (i < kNF) fr[i % kFragLead] = load(i);
+      if (i == kFragLead - 1) {
+        // row sums of exactly the bf16 weights that enter P V
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+          lsum[0] = mfma16(ones, __builtin_bit_cast(bf16x8, pw[kk][0]), lsum[0]);
+          lsum[1] = mfma16(ones, __builtin_bit_cast(bf16x8, pw[kk][1]), lsum[1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - 2 * kPairs, 0);
   };
 
   // One tile: t is the tile index; R = t mod 6 when it is known at compile
@@ -434,11 +439,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // the matrix half-step's wave issues first when both waves of the SIMD are
     // ready (MFMAs and operand reads ahead of the other wave's softmax VALU)
     __builtin_amdgcn_s_setprio(3);
-    pv(vslot(vp));
-    if constexpr (decltype(with_qk)::value) {
-      qk(kslot(kq));
-      schedule_matrix_half_step();
-    }
+    matrix_half_step(vslot(vp), kslot(kq), with_qk);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   };
