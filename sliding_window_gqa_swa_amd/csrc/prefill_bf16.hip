@@ -38,9 +38,10 @@
 //     mask code.  Keys outside the band are never read from outside it: their
 //     rows are loaded from the nearest key of the band (always written data)
 //     and masked, so unwritten cache slots cannot reach the arithmetic.
-//   * The matrix half-step is an explicit pipeline over operand fragments:
-//     each V or K fragment is read from LDS four fragments before the two
-//     MFMAs that use it, and every step of the pipeline is pinned in place.
+//   * The matrix half-step is an explicit pipeline over operand fragments
+//     (the next tile's K fragments, then this tile's V fragments): each is
+//     read from LDS three fragments before the two MFMAs that use it, and
+//     every step of the pipeline is pinned in place.
 //   * Online softmax in fp32 with exp2.  The softmax half-step competes with
 //     the other wave's MFMAs for the VALU issue port; it is kept small:
 //       - the score accumulators start at -M (the running max of q.k), so
@@ -379,34 +380,37 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
   const int n_diag_free = (q0 - kBN + 1 - kt0) >= 0 ? (q0 - kBN + 1 - kt0) / kBN + 1 : 0;
   const int t_mid_end = max(n_lead, min(n_tiles, n_diag_free));
 
-  // The matrix half-step M_t = { row sums; O^T += V^T P^T(t); S^T(t+1) - M =
-  // K(t+1) Q^T + negm } as a pipeline over operand fragments: first the 2 kDB V
-  // fragments (key slice kk, d-block db; two transposed reads each), then the
-  // 4 kKS K fragments (step ks, key block kbi; one read each), each feeding two
-  // MFMAs (query blocks 0 and 1).  Fragment f is read kFragLead fragments ahead
-  // of its MFMAs, the four row-sum MFMAs (no LDS operand) run under the latency
-  // of the first reads, and every iteration ends in a scheduling barrier, so
-  // the compiler keeps this order (its wait counts follow the reads).
-  constexpr int kFragLead = 4;
+  // The matrix half-step M_t = { row sums; S^T(t+1) - M = K(t+1) Q^T + negm;
+  // O^T += V^T P^T(t) } as a pipeline over operand fragments: first the 4 kKS K
+  // fragments of the next tile's scores (step ks, key block kbi; one read
+  // each), then the 2 kDB V fragments of P V (key slice kk, d-block db; two
+  // transposed reads each), each feeding two MFMAs (query blocks 0 and 1).  The
+  // scores come first because the next softmax half-step needs them; O is not
+  // read before the next matrix half-step.  Fragment f is read kFragLead
+  // fragments ahead of its MFMAs, the four row-sum MFMAs (no LDS operand) run
+  // under the latency of the first reads, and every iteration ends in a
+  // scheduling barrier, so the compiler keeps this order (its wait counts
+  // follow the reads).
+  constexpr int kFragLead = 3;
   auto matrix_half_step = [&](const unsigned char *vbase, const unsigned char *kb, auto with_qk)
                               __attribute__((always_inline)) {
-    constexpr int kNV = 2 * kDB;
-    constexpr int kNF = kNV + (decltype(with_qk)::value ? 4 * kKS : 0);
+    constexpr int kNK = decltype(with_qk)::value ? 4 * kKS : 0;
+    constexpr int kNF = kNK + 2 * kDB;
     bf16x8 fr[kFragLead];
     auto load = [&](int f) __attribute__((always_inline)) {
-      if (f < kNV) return vread(vbase, f / kDB, f % kDB);
-      const int g = f - kNV;
-      return *(const bf16x8 *)(kb + k_off[g / 4] + 16 * kRowB * (g % 4));
+      if (f < kNK) return *(const bf16x8 *)(kb + k_off[f / 4] + 16 * kRowB * (f % 4));
+      const int g = f - kNK;
+      return vread(vbase, g / kDB, g % kDB);
     };
     auto use = [&](int f, bf16x8 x) __attribute__((always_inline)) {
-      if (f < kNV) {
-        const int kk = f / kDB, db = f % kDB;
-        o[db][0] = mfma16(x, __builtin_bit_cast(bf16x8, pw[kk][0]), o[db][0]);
-        o[db][1] = mfma16(x, __builtin_bit_cast(bf16x8, pw[kk][1]), o[db][1]);
-      } else {
-        const int g = f - kNV, ks = g / 4, kbi = g % 4;
+      if (f < kNK) {
+        const int ks = f / 4, kbi = f % 4;
         sa[kbi][0] = mfma16(x, qf[ks][0], ks == 0 ? negm[0] : sa[kbi][0]);
         sa[kbi][1] = mfma16(x, qf[ks][1], ks == 0 ? negm[1] : sa[kbi][1]);
+      } else {
+        const int g = f - kNK, kk = g / kDB, db = g % kDB;
+        o[db][0] = mfma16(x, __builtin_bit_cast(bf16x8, pw[kk][0]), o[db][0]);
+        o[db][1] = mfma16(x, __builtin_bit_cast(bf16x8, pw[kk][1]), o[db][1]);
       }
     };
 #pragma unroll
