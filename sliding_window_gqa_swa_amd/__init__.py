@@ -76,6 +76,12 @@ def lib():
     if not os.path.exists(_LIB_PATH):
         raise SwaLibraryMissing(f"{_LIB_PATH} is missing: build it with "
                                 "`python -m sliding_window_gqa_swa_amd.build` (no fallback exists)")
+    # torch carries its own HIP runtime (SONAME libamdhip64.so.7) and loads it under
+    # another file name.  Loaded first, it satisfies libswa.so's dependency, so the
+    # library and torch share one runtime.  Loaded after libswa.so, it would come in
+    # as a second runtime, and the library's launches on torch's memory and streams
+    # would fail.
+    import torch  # noqa: F401
     L = ctypes.CDLL(_LIB_PATH)
     P = ctypes.POINTER
     L.swa_abi_version.restype = ctypes.c_int

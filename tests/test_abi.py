@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -33,6 +34,24 @@ def test_library_loads_and_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", swa.lib_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (swa_\w+)", out))
     assert set(names) <= exported
+
+
+def test_library_shares_torchs_hip_runtime_when_loaded_first():
+    """Loading libswa.so before anything has imported torch must still leave one HIP
+    runtime in the process: torch's own copy, which the library then uses.  A second
+    runtime would not know torch's device memory and streams."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import sliding_window_gqa_swa_amd as swa\n"
+            "swa.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    paths = eval(r.stdout.strip().splitlines()[-1])
+    import torch
+    assert len(paths) == 1, paths
+    assert os.path.dirname(paths[0]) == os.path.join(os.path.dirname(torch.__file__), "lib"), paths
 
 
 def test_abi_version_and_status_strings():
