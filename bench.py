@@ -261,18 +261,23 @@ def settle(fn, seconds: float) -> int:
                 return n
 
 
-def time_ms(fn, reps: int) -> float:
-    """Mean milliseconds of `fn` over `reps` launches, HIP events on the current stream
-    (after `settle`)."""
+def time_ms(fn, reps: int, windows: int = 3) -> float:
+    """Milliseconds per launch of `fn`, HIP events on the current stream (after `settle`):
+    the mean over `reps` back-to-back launches, taken in `windows` separate windows, and the
+    median of those means (a lone stall of the host or the part, tens of milliseconds, then
+    spoils one window instead of the figure)."""
     import torch
     settle(fn, SETTLE_S_SUITE)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    means = []
+    for _ in range(windows):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) / reps)
+    return sorted(means)[len(means) // 2]
 
 
 def time_ms_cold(fn, reps: int, flush) -> float:
@@ -343,6 +348,45 @@ def suite_causal_and_no_skip(pq, pk, pv, pout, scale, t_swa_ms, reps):
         "swa_vs_no_tile_skip_speedup_16k": round(t_noskip / t_swa_ms, 3),
         "causal_over_band_pairs_16k": round(band_pairs(0, n, n) / band_pairs(0, n, W), 3),
     }
+
+
+def suite_write_vs_copy(pcache, pbatch, pq, pk, pv, pout, scale, reps):
+    """The chunk's cache write against a plain device copy of the same bytes, each timed
+    alone right after the 16K prefill (the position it has in the step, where the prefill's
+    134 MB of output has just displaced the chunk's K/V from the Infinity Cache).  The write
+    moves the last min(C, W) tokens of K and of V; the copy, one contiguous device-to-device
+    copy in one launch, moves as many bytes from the end of the chunk's K (which the prefill
+    has just read too): the same bytes read and written, with no slot arithmetic."""
+    import torch
+    import sliding_window_gqa_swa_amd as swa
+    n = pk.shape[0]
+    rows = min(n, W, n // 2)
+    src = pk[n - 2 * rows:]
+    dst = torch.empty_like(src)
+    nbytes = 2 * src.numel() * src.element_size()
+    assert nbytes == 2 * 2 * min(n, W) * pk[0].numel() * pk.element_size()
+
+    def pre():
+        swa.swa_prefill_chunk(pcache, pbatch, pq, HQ, pk, pv, scale, pout)
+
+    def copy():
+        dst.copy_(src)
+
+    out = {}
+    for name, fn in (("cache_write", lambda: swa.swa_cache_write(pcache, pbatch, pk, pv)), ("device_copy", copy)):
+        settle(lambda: (pre(), fn()), SETTLE_S_SUITE)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            pre()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+        out[name] = {"us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    out["bytes"] = nbytes
+    out["write_over_copy_rate"] = round(out["device_copy"]["us"] / out["cache_write"]["us"], 3)
+    return {"chunk_write_vs_device_copy_after_prefill": out}
 
 
 def suite_chunked(up, scale, reps, cpu: bool):
@@ -705,6 +749,7 @@ def main():
     cpu = not args.no_cpu_baseline
     if not args.no_suite:
         s = suite_causal_and_no_skip(pq, pk, pv, pout, wp.scale, t_pre, reps=10)
+        s.update(suite_write_vs_copy(pcache, pbatch, pq, pk, pv, pout, wp.scale, reps=50))
         s.update(suite_chunked(up, scale, 10, cpu))
         s.update(suite_mixed(up, scale, 10, cpu))
         s.update(suite_decode_g1(scale, 20))
