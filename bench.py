@@ -24,7 +24,7 @@ fp64 oracle on the host cores: the whole 16K prefill, plus stated samples of
 the other workloads.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-suite]
-    python bench.py --only chunked|mixed|decode_g1   # one suite workload (for profilers)
+    python bench.py --only chunked|mixed|decode_g1|write_vs_copy   # one suite workload (for profilers)
 """
 from __future__ import annotations
 
@@ -611,7 +611,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-suite", action="store_true", help="skip the other workloads")
-    ap.add_argument("--only", choices=["chunked", "mixed", "decode_g1"],
+    ap.add_argument("--only", choices=["chunked", "mixed", "decode_g1", "write_vs_copy"],
                     help="run one suite workload alone and print its record (for profilers)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -634,10 +634,19 @@ def main():
     up = uploader(dev)
     scale = 1.0 / D ** 0.5
 
+    def write_vs_copy():
+        wp = mistral_prefill(1002, window=W, n=16384)
+        n = wp.seqs[0].n_new
+        pq, pk, pv = up(wp.q), up(wp.k_new), up(wp.v_new)
+        pout = torch.empty((n, HQ, D), dtype=torch.bfloat16, device=dev)
+        return suite_write_vs_copy(bf16_cache(1, HKV, W, dev), swa.Batch([n], [0], [0]), pq, pk, pv, pout,
+                                   wp.scale, 50)
+
     if args.only:
         fn = {"chunked": lambda: suite_chunked(up, scale, 5, False),
               "mixed": lambda: suite_mixed(up, scale, 5, False),
-              "decode_g1": lambda: suite_decode_g1(scale, 20)}[args.only]
+              "decode_g1": lambda: suite_decode_g1(scale, 20),
+              "write_vs_copy": write_vs_copy}[args.only]
         print(json.dumps({"only": args.only, **fn()}))
         return
 
