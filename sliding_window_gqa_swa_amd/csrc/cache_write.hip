@@ -15,15 +15,19 @@
 
 namespace swa {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kPiecesPerThread = 2;
 
 // Each thread streams pieces idx, idx + stride, ... of its sequence, issuing
 // the loads of the next piece before it stores the current one.  With one
 // piece per thread every wave loads, waits, then stores, so the launch reads
 // everything before it writes anything; two pieces per thread overlap the
-// second half's reads with the first half's writes (16K-token chunk after the
-// Infinity Cache was overwritten: 8.1 -> 7.0 us in the kernel).
+// second half's reads with the first half's writes.  The loads are ordinary
+// (cached) loads: the chunk's K/V were just read by the prefill of the same
+// chunk, and cached loads find them where non-temporal ones went to memory
+// (16384-token chunk right after its prefill: 11.0 -> 9.8 us between events).
+// 1024-thread workgroups, a quarter as many as with 256, measured fastest
+// there (256 x 4 or 512 x 2 or 4 pieces: 10.3-10.7 us).
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteParams p, int n_wg_x) {
   const int b = wg_y();
   const int32_t tok0 = p.seq.cu_seqlens[b];
@@ -48,14 +52,14 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteParams 
     return ((row * p.n_kv_heads + g) * p.window + (pos0 + tw) % p.window) * p.row_chunks + ch;
   };
 
-  u32x4 kx = __builtin_nontemporal_load(ksrc + idx);
-  u32x4 vx = __builtin_nontemporal_load(vsrc + idx);
+  u32x4 kx = ksrc[idx];
+  u32x4 vx = vsrc[idx];
   for (;;) {
     const int64_t nx = idx + stride;
     u32x4 kn = kx, vn = vx;
     if (nx < total) {
-      kn = __builtin_nontemporal_load(ksrc + nx);
-      vn = __builtin_nontemporal_load(vsrc + nx);
+      kn = ksrc[nx];
+      vn = vsrc[nx];
     }
     const int64_t d = dst_of(idx);
     ((u32x4 *)p.cache_k)[d] = kx;
