@@ -14,10 +14,13 @@ Hq * sum_i |J(i)|); the decode's K/V GB/s is reported beside it.  Each stage
 is timed with HIP events on the stream it runs on.  Before the warm-up steps,
 untimed steps run for 0.2 s: from idle, the part needs a few tens of
 milliseconds of load to reach the clock it holds under it, and every timing of
-the suite is preceded by 0.1 s of the same.
+the suite is preceded by 0.1 s of the same, and each suite timing is the
+median of three windows of back-to-back launches.
 
 The suite (default on) times the other workloads: causal attention and the
-prefill without its band tile skip at 16K tokens, 4 x 32768 tokens chunked
+prefill without its band tile skip at 16K tokens, the chunk's cache write
+against a plain device copy of the same bytes (both right after the prefill),
+4 x 32768 tokens chunked
 through the ring (and a chunk-size sweep), the ragged mixed batch, decode at
 G = 1, per-token decode steps, and a 32-layer ring.  The CPU baseline is the
 fp64 oracle on the host cores: the whole 16K prefill, plus stated samples of
