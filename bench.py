@@ -20,9 +20,8 @@ median of three windows of back-to-back launches.
 The suite (default on) times the other workloads: causal attention and the
 prefill without its band tile skip at 16K tokens, the chunk's cache write
 against a plain device copy of the same bytes (both right after the prefill),
-4 x 32768 tokens chunked
-through the ring (and a chunk-size sweep), the ragged mixed batch, decode at
-G = 1, per-token decode steps, and a 32-layer ring.  The CPU baseline is the
+4 x 32768 tokens chunked through the ring (and a chunk-size sweep), the ragged
+mixed batch, decode at G = 1, per-token decode steps, and a 32-layer ring.  The CPU baseline is the
 fp64 oracle on the host cores: the whole 16K prefill, plus stated samples of
 the other workloads.
 
